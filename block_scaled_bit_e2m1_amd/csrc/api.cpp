@@ -1,0 +1,178 @@
+// api.cpp -- the C ABI: argument validation, kernel-family dispatch, errors.
+//
+// Every check happens before any launch; a failing call launches nothing and
+// leaves a one-line reason in a thread-local buffer (bsq_last_error).  The
+// pages' CPU code panics on an unsupported scheme or a bad shape [rlx-cpu
+// quant.rs, compile_dequant_mat_mul and validate_dequant_matmul_dims]; a C ABI
+// cannot unwind, so those become status codes here.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/bsq.h"
+#include "bsq_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+bsq_status fail(bsq_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bsq_status ok() {
+  g_err[0] = 0;
+  return BSQ_OK;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bsq_status check_format(int fmt, int block) {
+  const int B = bsq::block_of(fmt);
+  if (!B) return fail(BSQ_ERR_UNSUPPORTED, "unknown format %d", fmt);
+  if (block != 0 && block != B)
+    return fail(BSQ_ERR_UNSUPPORTED, "format %d has block %d, got %d", fmt, B, block);
+  return BSQ_OK;
+}
+
+bsq_status check_shape(int fmt, int64_t n, int64_t k) {
+  if (n < 0 || k < 0) return fail(BSQ_ERR_ARG, "negative size n=%lld k=%lld", (long long)n, (long long)k);
+  const int B = bsq::block_of(fmt);
+  if (k % B) return fail(BSQ_ERR_SHAPE, "k=%lld is not a multiple of the block %d", (long long)k, B);
+  if (n > ((int64_t)1 << 40) / (k ? k : 1)) return fail(BSQ_ERR_SHAPE, "n*k too large");
+  return BSQ_OK;
+}
+
+size_t scale_elem_bytes(int fmt) {
+  switch (fmt) {
+    case bsq::kNVFP8: case bsq::kINT8_SYM: return 4;
+    case bsq::kINT4_AFFINE: return 2;
+    default: return 1;
+  }
+}
+
+bsq_status check_weight(int fmt, int64_t n, int64_t k, const void *codes, const void *scales, const void *biases) {
+  if (n == 0 || k == 0) return BSQ_OK;
+  if (!codes || !scales) return fail(BSQ_ERR_ARG, "null codes or scales");
+  if (fmt == bsq::kINT4_AFFINE && !biases) return fail(BSQ_ERR_ARG, "int4 affine needs biases");
+  if (!aligned(codes, 16)) return fail(BSQ_ERR_ALIGN, "codes must be 16-byte aligned");
+  if (!aligned(scales, scale_elem_bytes(fmt))) return fail(BSQ_ERR_ALIGN, "scales misaligned");
+  if (biases && !aligned(biases, 2)) return fail(BSQ_ERR_ALIGN, "biases misaligned");
+  return BSQ_OK;
+}
+
+bsq_status hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return ok();
+  return fail(BSQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bsq_status matmul(bsq_path path, bsq_format fmt, int block, int64_t m, int64_t n, int64_t k, const void *codes,
+                  const void *scales, const void *biases, float global_scale, const void *x, bsq_dtype xt,
+                  void *out, bsq_dtype ot, void *stream) {
+  bsq_status s;
+  if ((s = check_format(fmt, block))) return s;
+  if ((s = check_shape(fmt, n, k))) return s;
+  if (m < 0) return fail(BSQ_ERR_ARG, "negative m");
+  if (xt != BSQ_F32 && xt != BSQ_BF16) return fail(BSQ_ERR_ARG, "bad x dtype %d", (int)xt);
+  if (ot != BSQ_F32 && ot != BSQ_BF16) return fail(BSQ_ERR_ARG, "bad out dtype %d", (int)ot);
+  if (path != BSQ_PATH_AUTO && path != BSQ_PATH_ROWS && path != BSQ_PATH_MFMA)
+    return fail(BSQ_ERR_ARG, "bad path %d", (int)path);
+  if (path == BSQ_PATH_MFMA && xt != BSQ_BF16)
+    return fail(BSQ_ERR_UNSUPPORTED, "the MFMA path takes bf16 X");
+  if (m == 0 || n == 0) return ok();
+  if (!out) return fail(BSQ_ERR_ARG, "null out");
+  if (!aligned(out, ot == BSQ_F32 ? 4 : 2)) return fail(BSQ_ERR_ALIGN, "out misaligned");
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t ob = m * n * (ot == BSQ_F32 ? 4 : 2);
+  if (k == 0) return hip_status(bsq::launch_zero(out, ob, st), "zero-fill");
+  if ((s = check_weight(fmt, n, k, codes, scales, biases))) return s;
+  if (!x) return fail(BSQ_ERR_ARG, "null x");
+  if (!aligned(x, 16)) return fail(BSQ_ERR_ALIGN, "x must be 16-byte aligned");
+  if (m > ((int64_t)1 << 40) / k) return fail(BSQ_ERR_SHAPE, "m*k too large");
+  const bsq::QWeight w{(int)fmt, n, k, codes, scales, biases, global_scale};
+  if (path == BSQ_PATH_AUTO) path = (xt == BSQ_BF16 && m > 8) ? BSQ_PATH_MFMA : BSQ_PATH_ROWS;
+  if (path == BSQ_PATH_MFMA) return hip_status(bsq::launch_mfma(w, m, x, out, (int)ot, st), "mfma launch");
+  return hip_status(bsq::launch_rows(w, m, x, (int)xt, out, (int)ot, st), "rows launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+bsq_status bsq_packed_bytes(bsq_format fmt, int block, int64_t n, int64_t k, size_t *code_bytes,
+                            size_t *scale_bytes, size_t *bias_bytes) {
+  bsq_status s;
+  if ((s = check_format(fmt, block))) return s;
+  if ((s = check_shape(fmt, n, k))) return s;
+  const int64_t nb = n * (k / bsq::block_of(fmt));
+  if (code_bytes) *code_bytes = (size_t)(bsq::is_4bit(fmt) ? n * k / 2 : n * k);
+  if (scale_bytes) *scale_bytes = (size_t)nb * scale_elem_bytes(fmt);
+  if (bias_bytes) *bias_bytes = fmt == BSQ_INT4_AFFINE ? (size_t)nb * 2 : 0;
+  return ok();
+}
+
+bsq_status bsq_pack_host(bsq_format fmt, int block, const float *w, int64_t n, int64_t k, void *codes,
+                         void *scales, void *biases, float *global_out) {
+  bsq_status s;
+  if ((s = check_format(fmt, block))) return s;
+  if ((s = check_shape(fmt, n, k))) return s;
+  if (n * k > 0 && (!w || !codes || !scales)) return fail(BSQ_ERR_ARG, "null pointer");
+  if (n * k > 0 && fmt == BSQ_INT4_AFFINE && !biases) return fail(BSQ_ERR_ARG, "int4 affine needs biases");
+  const int st = bsq::pack_host(fmt, w, n, k, codes, scales, biases, global_out);
+  if (st) return fail((bsq_status)st, "non-finite weight value");
+  return ok();
+}
+
+bsq_status bsq_dequant(bsq_format fmt, int block, int64_t n, int64_t k, const void *codes, const void *scales,
+                       const void *biases, float global_scale, float *out, void *stream) {
+  bsq_status s;
+  if ((s = check_format(fmt, block))) return s;
+  if ((s = check_shape(fmt, n, k))) return s;
+  if (n == 0 || k == 0) return ok();
+  if ((s = check_weight(fmt, n, k, codes, scales, biases))) return s;
+  if (!out) return fail(BSQ_ERR_ARG, "null out");
+  if (!aligned(out, 16)) return fail(BSQ_ERR_ALIGN, "out must be 16-byte aligned");
+  const bsq::QWeight w{(int)fmt, n, k, codes, scales, biases, global_scale};
+  return hip_status(bsq::launch_dequant(w, out, (hipStream_t)stream), "dequant launch");
+}
+
+bsq_status bsq_qgemv(bsq_format fmt, int block, int64_t n, int64_t k, const void *codes, const void *scales,
+                     const void *biases, float global_scale, const void *x, bsq_dtype xt, void *out,
+                     bsq_dtype ot, void *stream) {
+  return matmul(BSQ_PATH_ROWS, fmt, block, 1, n, k, codes, scales, biases, global_scale, x, xt, out, ot, stream);
+}
+
+bsq_status bsq_qgemm(bsq_format fmt, int block, int64_t m, int64_t n, int64_t k, const void *codes,
+                     const void *scales, const void *biases, float global_scale, const void *x, bsq_dtype xt,
+                     void *out, bsq_dtype ot, void *stream) {
+  return matmul(BSQ_PATH_AUTO, fmt, block, m, n, k, codes, scales, biases, global_scale, x, xt, out, ot, stream);
+}
+
+bsq_status bsq_qgemm_path(bsq_path path, bsq_format fmt, int block, int64_t m, int64_t n, int64_t k,
+                          const void *codes, const void *scales, const void *biases, float global_scale,
+                          const void *x, bsq_dtype xt, void *out, bsq_dtype ot, void *stream) {
+  return matmul(path, fmt, block, m, n, k, codes, scales, biases, global_scale, x, xt, out, ot, stream);
+}
+
+const char *bsq_status_string(bsq_status s) {
+  switch (s) {
+    case BSQ_OK: return "ok";
+    case BSQ_ERR_ARG: return "invalid argument";
+    case BSQ_ERR_UNSUPPORTED: return "unsupported format or block";
+    case BSQ_ERR_SHAPE: return "unsupported shape";
+    case BSQ_ERR_ALIGN: return "misaligned pointer";
+    case BSQ_ERR_NONFINITE: return "non-finite input";
+    case BSQ_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char *bsq_last_error(void) { return g_err; }
+
+const char *bsq_version(void) { return "bsq 0.1.0 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// bsq_internal.hpp -- format traits and kernel launchers shared by the
+// library's translation units (not part of the public ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsq {
+
+enum Fmt : int {
+  kMXFP4 = 1,
+  kNVFP4 = 2,
+  kMXFP8_E4M3 = 3,
+  kMXFP8_E5M2 = 4,
+  kNVFP8 = 5,
+  kINT4_AFFINE = 6,
+  kINT8_SYM = 7
+};
+
+// Compile-time description of each format's storage.
+template <int F> struct Traits;
+template <> struct Traits<kMXFP4> { static constexpr int kBlock = 32, kBits = 4; };
+template <> struct Traits<kNVFP4> { static constexpr int kBlock = 16, kBits = 4; };
+template <> struct Traits<kMXFP8_E4M3> { static constexpr int kBlock = 32, kBits = 8; };
+template <> struct Traits<kMXFP8_E5M2> { static constexpr int kBlock = 32, kBits = 8; };
+template <> struct Traits<kNVFP8> { static constexpr int kBlock = 16, kBits = 8; };
+template <> struct Traits<kINT4_AFFINE> { static constexpr int kBlock = 64, kBits = 4; };
+template <> struct Traits<kINT8_SYM> { static constexpr int kBlock = 32, kBits = 8; };
+
+inline int block_of(int f) {
+  switch (f) {
+    case kMXFP4: case kMXFP8_E4M3: case kMXFP8_E5M2: case kINT8_SYM: return 32;
+    case kNVFP4: case kNVFP8: return 16;
+    case kINT4_AFFINE: return 64;
+    default: return 0;
+  }
+}
+inline bool is_4bit(int f) { return f == kMXFP4 || f == kNVFP4 || f == kINT4_AFFINE; }
+
+// A packed weight as the kernels see it (all device pointers).
+struct QWeight {
+  int fmt;
+  int64_t n, k;
+  const void *codes, *scales, *biases;
+  float global;
+};
+
+// Launchers (defined in the .hip files).  Shapes are validated by the caller.
+hipError_t launch_dequant(const QWeight &w, float *out, hipStream_t s);
+// VALU streaming kernel: any m, f32 or bf16 X (xt/ot: 0 = f32, 1 = bf16).
+hipError_t launch_rows(const QWeight &w, int64_t m, const void *x, int xt, void *out, int ot, hipStream_t s);
+// MFMA kernel: bf16 X, any m >= 1.
+hipError_t launch_mfma(const QWeight &w, int64_t m, const void *x, void *out, int ot, hipStream_t s);
+// Zero-fill an output of `bytes` bytes (k == 0 case).
+hipError_t launch_zero(void *out, int64_t bytes, hipStream_t s);
+
+// Host packer (pack_host.cpp).  Returns a bsq_status value.
+int pack_host(int fmt, const float *w, int64_t n, int64_t k, void *codes, void *scales, void *biases,
+              float *global_out);
+
+}  // namespace bsq

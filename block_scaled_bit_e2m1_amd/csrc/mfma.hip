@@ -1,0 +1,382 @@
+// mfma.hip -- prefill qgemm on gfx950 matrix cores (bf16 X):
+//   out[i,j] = sum_p X[i,p] * dequant(W)[j,p].
+//
+// This is the dense contraction of the method [metaltile PR #250,
+// "mt_mxfp4_qmm_mma" (the M >= 32 path) and the MMA commits for all formats;
+// metaltile-std src/mlx/fp_quantized_mma.rs, mt_fp4_qmm_mma: stage X and
+// dequantized W per k-block, then multiply-accumulate].  The Apple geometry
+// (32x32x32 tiles, 8x8 simdgroup fragments) is not used; the CDNA4 design:
+//
+//  * v_mfma_f32_32x32x16_bf16, fp32 accumulators in registers.  Operand
+//    layout for 32x32x16: lane l holds row/column l%32 and the 8 consecutive
+//    k values 8*(l/32)..8*(l/32)+7 of the 16-deep slice; the accumulator lane
+//    l holds column l%32, rows 8*(v/4) + 4*(l/32) + v%4 for v = 0..15.
+//  * A workgroup owns a BM x BN output tile; its waves split it WGM x WGN.
+//    The k loop steps BK = 64.  Inside a step the 16-deep MFMA slices are
+//    k-permuted: slice t, lane half h covers k = 32h + 8t + (0..7).  Both
+//    operands use the same permutation, so the sum is unchanged, and each
+//    lane's weight codes for a step are one contiguous 16-byte (4-bit) or
+//    32-byte (8-bit) run that maps straight onto its B-operand registers.
+//  * X (bf16) goes global -> registers -> LDS (double buffered, rows padded
+//    to 144 bytes so the 16-byte fragment reads are bank-conflict free) and
+//    is read back as A fragments.
+//  * W codes go global -> registers and are decoded there into bf16 B
+//    fragments, never touching LDS:
+//      mxfp4 / mxfp8:  v_cvt_scalef32_pk_bf16_{fp4,fp8,bf8} with the E8M0
+//                      scale (an exponent-only operand), exact in bf16;
+//      nvfp4:          e2m1 * e4m3 micro-scale in f32 (exact, <= 6 significant
+//                      bits) then bf16; the f32 global scales the accumulator
+//                      once at the end ("global scale multiplied once at the
+//                      end" [rlx-cpu quant.rs, dequant_matmul_nvfp4]);
+//      nvfp8 / int8 / int4: the f32 dequantized value w (one rounding, as the
+//                      standalone dequant) split into bf16 hi + lo, two MFMAs
+//                      per slice; |w - hi - lo| <= 2^-17 |w|.
+//  * Workgroup -> tile mapping is XCD-aware: consecutive workgroups are
+//    dispatched round-robin over the 8 XCDs, so tiles are renumbered to give
+//    each XCD a contiguous run of tiles that share X rows (one L2 per XCD).
+#include "bsq_internal.hpp"
+#include "codec.hpp"
+
+namespace bsq {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
+
+constexpr int BK = 64;
+constexpr int LDS_LD = BK + 8;  // bf16 per LDS row: 128 data bytes + 16 pad
+
+template <int F> constexpr bool kSplit = (F == kNVFP8 || F == kINT8_SYM || F == kINT4_AFFINE);
+
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};  // round to nearest even
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// hi = bf16(w), lo = bf16(w - hi) for two values; returns (hi pair, lo pair).
+__device__ __forceinline__ void split_pk(float a, float b, uint32_t &hi, uint32_t &lo) {
+  const __bf16 ha = (__bf16)a, hb = (__bf16)b;
+  const bf16x2_t h = {ha, hb};
+  const bf16x2_t l = {(__bf16)(a - (float)ha), (__bf16)(b - (float)hb)};
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+
+__device__ __forceinline__ bf16x8_t frag(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const uint4 u = make_uint4(a, b, c, d);
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
+// One lane's weight data for one BK step of one 32-column subtile.
+struct WRaw {
+  uint4 c0, c1;       // codes: c0 only for 4-bit; c0, c1 (32 bytes) for 8-bit
+  uint32_t s0, s1;    // raw scale bits (u8 E8M0/E4M3, f32 bits, bf16 bits)
+  uint32_t b0;        // int4 bias bits
+};
+
+template <int F, bool VEC>
+__device__ __forceinline__ void load_w(WRaw &r, const uint8_t *__restrict__ codes, const void *__restrict__ scales,
+                                       const uint16_t *__restrict__ biases, int64_t col, int64_t k, int64_t kbase,
+                                       bool tail) {
+  constexpr int B = Traits<F>::kBlock;
+  const int64_t nblk = k / B;
+  // kbase = k0 + 32h: this lane's 32 contiguous k values.
+  if constexpr (Traits<F>::kBits == 4) {
+    const uint8_t *p = codes + col * (k / 2) + kbase / 2;
+    if (VEC && !tail) {
+      r.c0 = *reinterpret_cast<const uint4 *>(p);
+    } else {
+      uint32_t t[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) t[q] = (kbase + 8 * q < k) ? reinterpret_cast<const uint32_t *>(p)[q] : 0u;
+      r.c0 = make_uint4(t[0], t[1], t[2], t[3]);
+    }
+    r.c1 = make_uint4(0, 0, 0, 0);
+  } else {
+    const uint8_t *p = codes + col * k + kbase;
+    if (!tail) {
+      r.c0 = reinterpret_cast<const uint4 *>(p)[0];
+      r.c1 = reinterpret_cast<const uint4 *>(p)[1];
+    } else {
+      uint32_t t[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) t[q] = (kbase + 4 * q < k) ? reinterpret_cast<const uint32_t *>(p)[q] : 0u;
+      r.c0 = make_uint4(t[0], t[1], t[2], t[3]);
+      r.c1 = make_uint4(t[4], t[5], t[6], t[7]);
+    }
+  }
+  int64_t b0 = kbase / B, b1 = (kbase + 16) / B;
+  if (tail) {
+    b0 = b0 < nblk ? b0 : nblk - 1;
+    b1 = b1 < nblk ? b1 : nblk - 1;
+  }
+  const int64_t s = col * nblk;
+  if constexpr (F == kMXFP4 || F == kNVFP4 || F == kMXFP8_E4M3 || F == kMXFP8_E5M2) {
+    const uint8_t *sp = reinterpret_cast<const uint8_t *>(scales) + s;
+    r.s0 = sp[b0];
+    r.s1 = (B == 16) ? sp[b1] : r.s0;
+  } else if constexpr (F == kNVFP8 || F == kINT8_SYM) {
+    const uint32_t *sp = reinterpret_cast<const uint32_t *>(scales) + s;
+    r.s0 = sp[b0];
+    r.s1 = (B == 16) ? sp[b1] : r.s0;
+  } else {
+    r.s0 = reinterpret_cast<const uint16_t *>(scales)[s + b0];
+    r.s1 = r.s0;
+    r.b0 = biases[s + b0];
+  }
+}
+
+// Build the B fragments (hi, and lo for split formats) of the 4 k-slices.
+template <int F>
+__device__ __forceinline__ void decode_w(const WRaw &r, bf16x8_t hi[4], bf16x8_t lo[4]) {
+  const uint32_t cw[8] = {r.c0.x, r.c0.y, r.c0.z, r.c0.w, r.c1.x, r.c1.y, r.c1.z, r.c1.w};
+  if constexpr (F == kMXFP4) {
+    const float sc = __uint_as_float(r.s0 << 23);  // exponent-only scale operand
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t w = cw[t];
+      hi[t] = frag(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3)));
+    }
+  } else if constexpr (F == kMXFP8_E4M3 || F == kMXFP8_E5M2) {
+    const float sc = __uint_as_float(r.s0 << 23);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t w0 = cw[2 * t], w1 = cw[2 * t + 1];
+      if constexpr (F == kMXFP8_E4M3) {
+        hi[t] = frag(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, false)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, true)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, false)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, true)));
+      } else {
+        hi[t] = frag(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w0, sc, false)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w0, sc, true)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w1, sc, false)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w1, sc, true)));
+      }
+    }
+  } else if constexpr (F == kNVFP4) {
+    const float m0 = e4m3_to_f32(r.s0), m1 = e4m3_to_f32(r.s1);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float ms = t < 2 ? m0 : m1;  // slices 0,1 in the first 16-block
+      const f32x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[t], 1.0f, 0);
+      const f32x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[t], 1.0f, 1);
+      const f32x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[t], 1.0f, 2);
+      const f32x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[t], 1.0f, 3);
+      // e2m1 * e4m3 has at most 6 significant bits: exact in f32 and in bf16
+      hi[t] = frag(pk_bf16(v0[0] * ms, v0[1] * ms), pk_bf16(v1[0] * ms, v1[1] * ms), pk_bf16(v2[0] * ms, v2[1] * ms),
+                   pk_bf16(v3[0] * ms, v3[1] * ms));
+    }
+  } else {
+    // split formats: w = f32 dequantized value, then hi/lo bf16
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float w[8];
+      if constexpr (F == kNVFP8) {
+        const float s = __uint_as_float(t < 2 ? r.s0 : r.s1);
+        const f32x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(cw[2 * t], 1.0f, false);
+        const f32x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(cw[2 * t], 1.0f, true);
+        const f32x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(cw[2 * t + 1], 1.0f, false);
+        const f32x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(cw[2 * t + 1], 1.0f, true);
+        const float e[8] = {v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[i] = e[i] * s;
+      } else if constexpr (F == kINT8_SYM) {
+        const float s = __uint_as_float(r.s0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t word = cw[2 * t + (i >> 2)];
+          const int q = (int)(int8_t)(uint8_t)(word >> (8 * (i & 3)));
+          w[i] = (float)q * s;
+        }
+      } else {  // int4 affine: s*q + b
+        const float s = bf16_bits_to_f32(r.s0), b = bf16_bits_to_f32(r.b0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[i] = __builtin_fmaf(s, (float)((cw[t] >> (4 * i)) & 0xFu), b);
+      }
+      uint32_t h[4], l[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) split_pk(w[2 * i], w[2 * i + 1], h[i], l[i]);
+      hi[t] = frag(h[0], h[1], h[2], h[3]);
+      lo[t] = frag(l[0], l[1], l[2], l[3]);
+    }
+  }
+}
+
+template <int F, int BM, int BN, int WGM, int WGN, bool VEC>
+__global__ void __launch_bounds__(WGM *WGN * 64)
+mfma_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, const uint16_t *__restrict__ biases,
+            float global, const uint16_t *__restrict__ x, void *__restrict__ out, int ot, int64_t m, int64_t n,
+            int64_t k, int tiles_m, int tiles_n) {
+  constexpr int NTHR = WGM * WGN * 64;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int MT = WTM / 32, NT = WTN / 32;
+  constexpr int XCH = BM * (BK / 8) / NTHR;  // 16-byte X chunks per thread per step
+  static_assert(XCH * NTHR == BM * (BK / 8), "X tile must split evenly");
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * LDS_LD];
+
+  // ---- tile mapping: contiguous tile runs per XCD ----
+  const int T = tiles_m * tiles_n;
+  int t = blockIdx.x;
+  if ((T & 7) == 0) t = (t & 7) * (T >> 3) + (t >> 3);
+  const int tm = t / tiles_n, tn = t - tm * tiles_n;
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid / WGN, wn = wid - (wid / WGN) * WGN;
+  const int l32 = lane & 31, h = lane >> 5;
+
+  // X chunk c of this thread: row c / 8, 8-element column group c % 8.
+  int64_t xrow[XCH];
+  int xcol[XCH];
+#pragma unroll
+  for (int c = 0; c < XCH; ++c) {
+    const int cid = c * NTHR + tid;
+    const int r = cid >> 3;
+    int64_t gr = m0 + r;
+    xrow[c] = gr < m ? gr : m - 1;  // rows past m read a valid row; never stored
+    xcol[c] = (cid & 7) * 8;
+  }
+  int64_t wcol[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int64_t gc = n0 + wn * WTN + j * 32 + l32;
+    wcol[j] = gc < n ? gc : n - 1;
+  }
+
+  f32x16_t acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  const int KT = (int)((k + BK - 1) / BK);
+  uint4 xr[XCH];
+  WRaw wr[NT];
+
+  auto load_x = [&](int kt, bool tail) {
+    const int64_t k0 = (int64_t)kt * BK;
+#pragma unroll
+    for (int c = 0; c < XCH; ++c) {
+      const int64_t kk = k0 + xcol[c];
+      if (!tail || kk < k)
+        xr[c] = *reinterpret_cast<const uint4 *>(x + xrow[c] * k + kk);
+      else
+        xr[c] = make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_x = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < XCH; ++c) {
+      const int cid = c * NTHR + tid;
+      *reinterpret_cast<uint4 *>(&xs[buf][(cid >> 3) * LDS_LD + (cid & 7) * 8]) = xr[c];
+    }
+  };
+  auto load_ws = [&](int kt, bool tail) {
+    const int64_t kb = (int64_t)kt * BK + 32 * h;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) load_w<F, VEC>(wr[j], codes, scales, biases, wcol[j], k, kb, tail);
+  };
+
+  load_x(0, KT == 1);
+  load_ws(0, KT == 1);
+  store_x(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    bf16x8_t bh[NT][4], bl[NT][4];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) decode_w<F>(wr[j], bh[j], bl[j]);
+    const bool more = kt + 1 < KT;
+    if (more) {
+      const bool tail = kt + 2 == KT && (k % BK) != 0;
+      load_x(kt + 1, tail);
+      load_ws(kt + 1, tail);
+    }
+    const uint16_t *xb = xs[cur];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        const int row = wm * WTM + i * 32 + l32;
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(&xb[row * LDS_LD + 32 * h + 8 * s]);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh[j][s], acc[i][j], 0, 0, 0);
+          if constexpr (kSplit<F>) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl[j][s], acc[i][j], 0, 0, 0);
+        }
+      }
+    }
+    if (more) store_x(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue ----
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int64_t col = n0 + wn * WTN + j * 32 + l32;
+      if (col >= n) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t row = m0 + wm * WTM + i * 32 + (v >> 2) * 8 + h * 4 + (v & 3);
+        if (row >= m) continue;
+        float val = acc[i][j][v];
+        if constexpr (F == kNVFP4) val *= global;
+        if (ot == 0) reinterpret_cast<float *>(out)[row * n + col] = val;
+        else reinterpret_cast<uint16_t *>(out)[row * n + col] = f32_to_bf16_bits(val);
+      }
+    }
+  }
+}
+
+template <int F, int BM, int BN, int WGM, int WGN>
+hipError_t run_cfg(const QWeight &w, int64_t m, const void *x, void *out, int ot, hipStream_t s) {
+  const int tiles_m = (int)((m + BM - 1) / BM), tiles_n = (int)((w.n + BN - 1) / BN);
+  const dim3 grid((unsigned)(tiles_m * tiles_n));
+  const bool vec = Traits<F>::kBits == 8 || (w.k % 32) == 0;
+  if (vec)
+    hipLaunchKernelGGL((mfma_kernel<F, BM, BN, WGM, WGN, true>), grid, dim3(WGM * WGN * 64), 0, s,
+                       (const uint8_t *)w.codes, w.scales, (const uint16_t *)w.biases, w.global, (const uint16_t *)x,
+                       out, ot, m, w.n, w.k, tiles_m, tiles_n);
+  else
+    hipLaunchKernelGGL((mfma_kernel<F, BM, BN, WGM, WGN, false>), grid, dim3(WGM * WGN * 64), 0, s,
+                       (const uint8_t *)w.codes, w.scales, (const uint16_t *)w.biases, w.global, (const uint16_t *)x,
+                       out, ot, m, w.n, w.k, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+template <int F>
+hipError_t run_f(const QWeight &w, int64_t m, const void *x, void *out, int ot, hipStream_t s) {
+  if ((m + 127) / 128 * ((w.n + 127) / 128) > (int64_t)1 << 30) return hipErrorInvalidValue;
+  // 256x128 tiles when they fill the chip, 128x128 otherwise.
+  const int64_t big = ((m + 255) / 256) * ((w.n + 127) / 128);
+  if (big >= 256) return run_cfg<F, 256, 128, 2, 2>(w, m, x, out, ot, s);
+  return run_cfg<F, 128, 128, 2, 2>(w, m, x, out, ot, s);
+}
+
+}  // namespace
+
+hipError_t launch_mfma(const QWeight &w, int64_t m, const void *x, void *out, int ot, hipStream_t s) {
+  switch (w.fmt) {
+    case kMXFP4: return run_f<kMXFP4>(w, m, x, out, ot, s);
+    case kNVFP4: return run_f<kNVFP4>(w, m, x, out, ot, s);
+    case kMXFP8_E4M3: return run_f<kMXFP8_E4M3>(w, m, x, out, ot, s);
+    case kMXFP8_E5M2: return run_f<kMXFP8_E5M2>(w, m, x, out, ot, s);
+    case kNVFP8: return run_f<kNVFP8>(w, m, x, out, ot, s);
+    case kINT4_AFFINE: return run_f<kINT4_AFFINE>(w, m, x, out, ot, s);
+    case kINT8_SYM: return run_f<kINT8_SYM>(w, m, x, out, ot, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace bsq

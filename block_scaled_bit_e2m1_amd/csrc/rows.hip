@@ -1,0 +1,274 @@
+// rows.hip -- VALU streaming kernel for the decode GEMV (m = 1) and for small
+// m / f32 activations: out[i,j] = sum_p X[i,p] * dequant(W)[j,p].
+//
+// The weight stream is the cost ("the win is memory bandwidth, not flops,
+// since LLM weights dominate the working set" [rlx-cpu quant.rs,
+// dequant_matmul_int8]), so each weight row is read from HBM once per launch
+// with 16-byte loads and decoded in registers; every X row of the launch's
+// m-chunk reuses the decoded codes.
+//
+// Geometry (gfx950, wave64): a wave owns one weight row at a time.  Lane l
+// takes 16-byte code chunks l, l+64, l+128, ... along k (32 elements for 4-bit
+// codes, 16 for 8-bit).  Up to kUnroll chunks are loaded before any is used,
+// so a wave keeps several HBM requests in flight.  Per 8-element sub-chunk the
+// unscaled element values are dotted with X in fp32; the block scale is folded
+// once per block ("fold in that block's scale ONCE (not per element)" [rlx-cpu
+// quant.rs, dequant_matmul_int8]) and the nvfp4 global once at the end
+// [rlx-cpu quant.rs, dequant_matmul_nvfp4].  int4 affine folds s and b per
+// group as s * sum(q*x) + b * sum(x) [metaltile-std tests/qmm_gpu_correctness.rs,
+// cpu_qmm_reference].  The wave's partial sums are reduced with DPP row
+// permutes and two cross-row swaps.
+//
+// bf16 X uses the gfx950 conversions (v_cvt_scalef32_pk_bf16_fp4/fp8/bf8 with
+// scale 1.0, which are exact for these element sets) and v_dot2_f32_bf16; f32
+// X and the integer formats use the branch-free software decoders and fp32 FMA.
+#include "bsq_internal.hpp"
+#include "codec.hpp"
+
+namespace bsq {
+namespace {
+
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2_t, u); }
+
+// Sum over the 64 lanes of a wave; every lane receives the total.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));  // half-row mirror
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));  // row mirror
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+// Unscaled element values of one 8-element sub-chunk (software decoders).
+template <int F>
+__device__ __forceinline__ void decode8(uint32_t w0, uint32_t w1, float e[8]) {
+  if constexpr (Traits<F>::kBits == 4) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t c = (w0 >> (4 * i)) & 0xFu;
+      if constexpr (F == kINT4_AFFINE) e[i] = (float)c;
+      else e[i] = e2m1_to_f32(c);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t c = ((i < 4 ? w0 : w1) >> (8 * (i & 3))) & 0xFFu;
+      if constexpr (F == kMXFP8_E4M3 || F == kNVFP8) e[i] = e4m3_to_f32(c);
+      else if constexpr (F == kMXFP8_E5M2) e[i] = e5m2_to_f32(c);
+      else e[i] = (float)(int8_t)(uint8_t)c;
+    }
+  }
+}
+
+// acc + sum_i elem_i * x_i for 8 elements with bf16 x (packed pairs in xv).
+template <int F>
+__device__ __forceinline__ float dot8_bf16(uint32_t w0, uint32_t w1, uint4 xv, float acc) {
+  if constexpr (F == kMXFP4 || F == kNVFP4) {
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w0, 1.0f, 0), as_bf16x2(xv.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w0, 1.0f, 1), as_bf16x2(xv.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w0, 1.0f, 2), as_bf16x2(xv.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w0, 1.0f, 3), as_bf16x2(xv.w), acc, false);
+    return acc;
+  } else if constexpr (F == kMXFP8_E4M3 || F == kNVFP8) {
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false), as_bf16x2(xv.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true), as_bf16x2(xv.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false), as_bf16x2(xv.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true), as_bf16x2(xv.w), acc, false);
+    return acc;
+  } else if constexpr (F == kMXFP8_E5M2) {
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w0, 1.0f, false), as_bf16x2(xv.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w0, 1.0f, true), as_bf16x2(xv.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w1, 1.0f, false), as_bf16x2(xv.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w1, 1.0f, true), as_bf16x2(xv.w), acc, false);
+    return acc;
+  } else {
+    float e[8];
+    decode8<F>(w0, w1, e);
+    const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc = __builtin_fmaf(e[2 * i], __uint_as_float(xs[i] << 16), acc);
+      acc = __builtin_fmaf(e[2 * i + 1], __uint_as_float(xs[i] & 0xFFFF0000u), acc);
+    }
+    return acc;
+  }
+}
+
+template <int F>
+__device__ __forceinline__ float dot8_f32(uint32_t w0, uint32_t w1, const float x[8], float acc) {
+  float e[8];
+  decode8<F>(w0, w1, e);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc = __builtin_fmaf(e[i], x[i], acc);
+  return acc;
+}
+
+// Block scale of row j, block b as f32 (bias separately for int4).
+template <int F>
+__device__ __forceinline__ float load_scale(const void *scales, int64_t idx) {
+  if constexpr (F == kMXFP4 || F == kMXFP8_E4M3 || F == kMXFP8_E5M2)
+    return e8m0_to_f32(reinterpret_cast<const uint8_t *>(scales)[idx]);
+  else if constexpr (F == kNVFP4) return e4m3_to_f32(reinterpret_cast<const uint8_t *>(scales)[idx]);
+  else if constexpr (F == kNVFP8 || F == kINT8_SYM) return reinterpret_cast<const float *>(scales)[idx];
+  else return bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(scales)[idx]);
+}
+
+constexpr int kWaves = 4;   // waves per workgroup
+constexpr int kUnroll = 4;  // 16-byte code chunks loaded per lane before use
+
+template <int F, int M, int XT, bool VEC>
+__global__ void __launch_bounds__(kWaves * 64)
+rows_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, const uint16_t *__restrict__ biases,
+            float global, const void *__restrict__ xv, void *__restrict__ out, int ot, int64_t m, int64_t n, int64_t k) {
+  constexpr int B = Traits<F>::kBlock;
+  constexpr int E = Traits<F>::kBits == 4 ? 32 : 16;  // elements per 16-byte chunk
+  constexpr int NSUB = E / 8;                           // 8-element sub-chunks per chunk
+  constexpr int NB = B < E ? E / B : 1;                 // scale blocks per chunk
+  constexpr int SPB = NSUB / NB;                        // sub-chunks per scale block
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * kWaves;
+  const int64_t i0 = (int64_t)blockIdx.y * M;  // first X row of this launch chunk
+  const int64_t nblk = k / B;
+  const int64_t row_bytes = Traits<F>::kBits == 4 ? k / 2 : k;
+
+  for (int64_t j = wave; j < n; j += nwaves) {
+    float acc[M];
+#pragma unroll
+    for (int mi = 0; mi < M; ++mi) acc[mi] = 0.0f;
+    const uint8_t *crow = codes + j * row_bytes;
+
+    for (int64_t kc0 = (int64_t)lane * E; kc0 < k; kc0 += (int64_t)64 * E * kUnroll) {
+      uint4 cw[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t kc = kc0 + (int64_t)u * 64 * E;
+        const int64_t off = Traits<F>::kBits == 4 ? kc / 2 : kc;
+        if (VEC && kc + E <= k) {
+          cw[u] = *reinterpret_cast<const uint4 *>(crow + off);
+        } else {
+          uint32_t t[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (kc + (int64_t)(q + 1) * E / 4 <= k) t[q] = reinterpret_cast<const uint32_t *>(crow + off)[q];
+          cw[u] = make_uint4(t[0], t[1], t[2], t[3]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t kc = kc0 + (int64_t)u * 64 * E;
+        if (kc >= k) break;
+        const uint32_t cwa[4] = {cw[u].x, cw[u].y, cw[u].z, cw[u].w};
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const int64_t pb = kc + (int64_t)b * (E / NB);
+          if (pb >= k) break;
+          const float sc = load_scale<F>(scales, j * nblk + pb / B);
+          float bias = 0.0f;
+          if constexpr (F == kINT4_AFFINE) bias = bf16_bits_to_f32(biases[j * nblk + pb / B]);
+          float part[M], xsum[M];
+#pragma unroll
+          for (int mi = 0; mi < M; ++mi) part[mi] = xsum[mi] = 0.0f;
+#pragma unroll
+          for (int s = b * SPB; s < (b + 1) * SPB; ++s) {
+            const int64_t p = kc + 8 * s;
+            if (p >= k) break;
+            // code words of this sub-chunk: one word (4-bit) or two (8-bit)
+            const uint32_t w0 = Traits<F>::kBits == 4 ? cwa[s] : cwa[2 * s];
+            const uint32_t w1 = Traits<F>::kBits == 4 ? 0u : cwa[2 * s + 1];
+#pragma unroll
+            for (int mi = 0; mi < M; ++mi) {
+              if (i0 + mi >= m) break;
+              if constexpr (XT == 1) {
+                const uint4 xq = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(xv) + (i0 + mi) * k + p);
+                part[mi] = dot8_bf16<F>(w0, w1, xq, part[mi]);
+                if constexpr (F == kINT4_AFFINE) {
+                  const uint32_t xs[4] = {xq.x, xq.y, xq.z, xq.w};
+#pragma unroll
+                  for (int i = 0; i < 4; ++i)
+                    xsum[mi] += __uint_as_float(xs[i] << 16) + __uint_as_float(xs[i] & 0xFFFF0000u);
+                }
+              } else {
+                const float4 *xp = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(xv) + (i0 + mi) * k + p);
+                const float4 a = xp[0], c = xp[1];
+                const float xf[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+                part[mi] = dot8_f32<F>(w0, w1, xf, part[mi]);
+                if constexpr (F == kINT4_AFFINE) {
+#pragma unroll
+                  for (int i = 0; i < 8; ++i) xsum[mi] += xf[i];
+                }
+              }
+            }
+          }
+#pragma unroll
+          for (int mi = 0; mi < M; ++mi) {
+            acc[mi] = __builtin_fmaf(part[mi], sc, acc[mi]);
+            if constexpr (F == kINT4_AFFINE) acc[mi] = __builtin_fmaf(xsum[mi], bias, acc[mi]);
+          }
+        }
+      }
+    }
+
+#pragma unroll
+    for (int mi = 0; mi < M; ++mi) {
+      float v = wave_sum(acc[mi]);
+      if constexpr (F == kNVFP4) v *= global;
+      if (lane == mi && i0 + mi < m) {
+        const int64_t o = (i0 + mi) * n + j;
+        if (ot == 0) reinterpret_cast<float *>(out)[o] = v;
+        else reinterpret_cast<uint16_t *>(out)[o] = f32_to_bf16_bits(v);
+      }
+    }
+  }
+}
+
+template <int F, int M, int XT>
+hipError_t run_m(const QWeight &w, int64_t m, const void *x, void *out, int ot, hipStream_t s) {
+  const bool vec = Traits<F>::kBits == 8 || (w.k % 32) == 0;  // 16-byte aligned code rows
+  int64_t wgs = (w.n + kWaves - 1) / kWaves;
+  if (wgs > 8192) wgs = 8192;
+  const int64_t ychunks = (m + M - 1) / M;
+  const dim3 grid((unsigned)wgs, (unsigned)ychunks);
+  if (vec)
+    hipLaunchKernelGGL((rows_kernel<F, M, XT, true>), grid, dim3(kWaves * 64), 0, s, (const uint8_t *)w.codes,
+                       w.scales, (const uint16_t *)w.biases, w.global, x, out, ot, m, w.n, w.k);
+  else
+    hipLaunchKernelGGL((rows_kernel<F, M, XT, false>), grid, dim3(kWaves * 64), 0, s, (const uint8_t *)w.codes,
+                       w.scales, (const uint16_t *)w.biases, w.global, x, out, ot, m, w.n, w.k);
+  return hipGetLastError();
+}
+
+template <int F, int XT>
+hipError_t run_x(const QWeight &w, int64_t m, const void *x, void *out, int ot, hipStream_t s) {
+  if (m <= 1) return run_m<F, 1, XT>(w, m, x, out, ot, s);
+  if (m <= 2) return run_m<F, 2, XT>(w, m, x, out, ot, s);
+  if (m <= 4) return run_m<F, 4, XT>(w, m, x, out, ot, s);
+  return run_m<F, 8, XT>(w, m, x, out, ot, s);
+}
+
+template <int F>
+hipError_t run_f(const QWeight &w, int64_t m, const void *x, int xt, void *out, int ot, hipStream_t s) {
+  if (m > (int64_t)65535 * 8) return hipErrorInvalidValue;
+  return xt == 1 ? run_x<F, 1>(w, m, x, out, ot, s) : run_x<F, 0>(w, m, x, out, ot, s);
+}
+
+}  // namespace
+
+hipError_t launch_rows(const QWeight &w, int64_t m, const void *x, int xt, void *out, int ot, hipStream_t s) {
+  switch (w.fmt) {
+    case kMXFP4: return run_f<kMXFP4>(w, m, x, xt, out, ot, s);
+    case kNVFP4: return run_f<kNVFP4>(w, m, x, xt, out, ot, s);
+    case kMXFP8_E4M3: return run_f<kMXFP8_E4M3>(w, m, x, xt, out, ot, s);
+    case kMXFP8_E5M2: return run_f<kMXFP8_E5M2>(w, m, x, xt, out, ot, s);
+    case kNVFP8: return run_f<kNVFP8>(w, m, x, xt, out, ot, s);
+    case kINT4_AFFINE: return run_f<kINT4_AFFINE>(w, m, x, xt, out, ot, s);
+    case kINT8_SYM: return run_f<kINT8_SYM>(w, m, x, xt, out, ot, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace bsq

@@ -1,0 +1,151 @@
+/*
+ * bsq.h -- block-scaled quantized matmul for AMD Instinct MI355X (gfx950).
+ *
+ * out[i,j] = sum_p X[i,p] * dequant(W)[j,p]
+ *
+ * where W is stored as packed low-bit element codes plus one scale per block
+ * of consecutive elements along k.  Plain C ABI: every entry point returns a
+ * bsq_status, none aborts, throws or allocates caller-visible memory.
+ *
+ * Formats (element x block x scale), as the pages define them
+ * [metaltile PR #250, "complete op x quant-format matrix", table of spec float
+ *  formats and commits "Foundation for the spec-conformant ... formats" and
+ *  "QFormat {Nvfp4, Mxfp4, Mxfp8E4, Mxfp8E5, Nvfp8} with pack() and dequant()";
+ *  metaltile-std tests/qmm_gpu_correctness.rs, int4 affine reference]:
+ *
+ *   BSQ_MXFP4       E2M1, block 32, E8M0 scale 2^(b-127)
+ *   BSQ_NVFP4       E2M1, block 16, E4M3 micro-scale x one f32 global
+ *   BSQ_MXFP8_E4M3  E4M3, block 32, E8M0
+ *   BSQ_MXFP8_E5M2  E5M2, block 32, E8M0
+ *   BSQ_NVFP8       E4M3, block 16, f32 scale
+ *   BSQ_INT4_AFFINE unsigned 4-bit q, group 64, value s*q + b (bf16 s and b)
+ *   BSQ_INT8_SYM    signed 8-bit q in [-127,127], block 32, f32 scale
+ *
+ * Stored layouts (all row-major, k contiguous; element (j,p) of W):
+ *   4-bit codes: u32 words [n, k/8]; element p sits in word p/8 at bits
+ *                4*(p%8)..4*(p%8)+3 (LSB first, low nibble = even element)
+ *                [metaltile-std src/mlx/fp_quantized_mma.rs, "W coop-dequant";
+ *                 rlx-cpu quant.rs, dequant_matmul_int4 nibble order].
+ *   8-bit codes: one byte per element, [n, k].
+ *   scales:      [n, k/block]: u8 (E8M0, E4M3), f32 (nvfp8, int8), bf16 bits
+ *                as u16 (int4).  int4 biases: bf16 [n, k/64].
+ *   X: [m, k] f32 or bf16.  out: [m, n] f32 or bf16 (round to nearest even).
+ *
+ * Shapes: k must be a multiple of the format's block (BSQ_ERR_SHAPE otherwise);
+ * m, n, k may be 0 (nothing is launched; for k == 0 the output is zero-filled).
+ * Pointers: device pointers (hipMalloc / torch CUDA tensors) unless marked
+ * host.  Codes and X must be 16-byte aligned, out and scales aligned to their
+ * element size (BSQ_ERR_ALIGN otherwise).  The caller owns every buffer; the
+ * library keeps no state between calls other than the thread-local error text.
+ * Device work is enqueued asynchronously on `stream` (a hipStream_t; NULL is
+ * the default stream); errors detected before launch are returned
+ * synchronously, launch failures as BSQ_ERR_HIP.
+ */
+#ifndef BSQ_H
+#define BSQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BSQ_OK = 0,
+    BSQ_ERR_ARG = 1,         /* null pointer, negative size, bad dtype */
+    BSQ_ERR_UNSUPPORTED = 2, /* unknown format, or block != the format's block */
+    BSQ_ERR_SHAPE = 3,       /* k not a multiple of the block, or sizes overflow */
+    BSQ_ERR_ALIGN = 4,       /* pointer misaligned for the kernel's vector loads */
+    BSQ_ERR_NONFINITE = 5,   /* pack input holds NaN or inf */
+    BSQ_ERR_HIP = 6          /* HIP launch / runtime error (see bsq_last_error) */
+} bsq_status;
+
+typedef enum {
+    BSQ_MXFP4 = 1,
+    BSQ_NVFP4 = 2,
+    BSQ_MXFP8_E4M3 = 3,
+    BSQ_MXFP8_E5M2 = 4,
+    BSQ_NVFP8 = 5,
+    BSQ_INT4_AFFINE = 6,
+    BSQ_INT8_SYM = 7
+} bsq_format;
+
+typedef enum { BSQ_F32 = 0, BSQ_BF16 = 1 } bsq_dtype;
+
+/* Kernel family selector for bsq_qgemm_path. */
+typedef enum {
+    BSQ_PATH_AUTO = 0,  /* library choice by shape and dtype */
+    BSQ_PATH_ROWS = 1,  /* VALU streaming kernel: W decoded once, FMA against every X row */
+    BSQ_PATH_MFMA = 2   /* LDS-tiled bf16 MFMA kernel (bf16 X only) */
+} bsq_path;
+
+/* Byte sizes of the packed representation of an [n,k] weight
+ * ("byte-layout sizes" [metaltile PR #250, format tests]).  `block` is 0 for
+ * the format's block or must equal it.  Any output pointer may be NULL. */
+bsq_status bsq_packed_bytes(bsq_format fmt, int block, int64_t n, int64_t k, size_t *code_bytes,
+                            size_t *scale_bytes, size_t *bias_bytes);
+
+/* Host packer: f32 weights (host [n,k]) -> codes + scales (+ int4 biases,
+ * + nvfp4 global), all host buffers sized by bsq_packed_bytes.
+ * Per block along k: the scale is chosen from the block amax (OCP shared
+ * exponent for E8M0; nvfp4 two-level global f32(T/2688) with E4M3 micro-scale
+ * amax_b/(6g); f32 amax/448 for nvfp8 and amax/127 for int8; bf16 min/max for
+ * int4), then every element is encoded against the scale as stored
+ * ("pack quantizes against the effective (post-encode) scale"), nearest with
+ * ties to even, saturating at the element's largest finite value
+ * [metaltile PR #250, QFormat pack commit; rlx-cpu quant.rs,
+ *  lowp_compute_scales / lowp_quantize].  `biases` is required for int4 only;
+ * `global_out` (may be NULL) receives the nvfp4 global (1.0 otherwise).
+ * Returns BSQ_ERR_NONFINITE if w holds NaN or inf (outputs then undefined). */
+bsq_status bsq_pack_host(bsq_format fmt, int block, const float *w, int64_t n, int64_t k, void *codes,
+                         void *scales, void *biases, float *global_out);
+
+/* Standalone dequant: out (device f32 [n,k]) = decode(code) * scale with one
+ * rounding to f32 (nvfp4: (e2m1 * e4m3) * global; int4: s*q + b)
+ * [metaltile PR #250, "First spec-conformant block-scaled dequant kernel" and
+ *  the commit completing the standalone dequant kernels].  Bit-exact against
+ * the CPU definition, NaN and -0 included.  out must be 16-byte aligned. */
+bsq_status bsq_dequant(bsq_format fmt, int block, int64_t n, int64_t k, const void *codes,
+                       const void *scales, const void *biases, float global_scale, float *out,
+                       void *stream);
+
+/* Decode GEMV (m = 1): out[j] = sum_p x[p] * dequant(W)[j,p], fp32
+ * accumulation, per-block scale folded once per block and the nvfp4 global
+ * once at the end [metaltile PR #250, "First block-scaled matmul kernel:
+ * mt_mxfp4_qgemv"; rlx-cpu quant.rs, dequant_matmul_nvfp4].
+ * x: device [k] (xt), out: device [n] (ot). */
+bsq_status bsq_qgemv(bsq_format fmt, int block, int64_t n, int64_t k, const void *codes, const void *scales,
+                     const void *biases, float global_scale, const void *x, bsq_dtype xt, void *out,
+                     bsq_dtype ot, void *stream);
+
+/* Multi-row quantized matmul: out[i,j] = sum_p X[i,p] * dequant(W)[j,p]
+ * [metaltile PR #250, qmm commit and "mt_mxfp4_qmm_mma" (the M >= 32 path);
+ *  metaltile-std src/mlx/fp_quantized_mma.rs, mt_fp4_qmm_mma].  Small m and
+ * f32 X use the streaming kernel, larger bf16 m the MFMA kernel. */
+bsq_status bsq_qgemm(bsq_format fmt, int block, int64_t m, int64_t n, int64_t k, const void *codes,
+                     const void *scales, const void *biases, float global_scale, const void *x, bsq_dtype xt,
+                     void *out, bsq_dtype ot, void *stream);
+
+/* bsq_qgemm with an explicit kernel family (for cross-path checks: the m = 1
+ * result of either family must agree with bsq_qgemv [metaltile-std
+ * tests/qmm_gpu_correctness.rs, m=1 qmm vs qmv test]).  BSQ_PATH_MFMA with f32
+ * X returns BSQ_ERR_UNSUPPORTED. */
+bsq_status bsq_qgemm_path(bsq_path path, bsq_format fmt, int block, int64_t m, int64_t n, int64_t k,
+                          const void *codes, const void *scales, const void *biases, float global_scale,
+                          const void *x, bsq_dtype xt, void *out, bsq_dtype ot, void *stream);
+
+/* Static text for a status code. */
+const char *bsq_status_string(bsq_status s);
+
+/* Detail of the last failing call on this thread ("" if none). */
+const char *bsq_last_error(void);
+
+/* Library version string. */
+const char *bsq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSQ_H */

@@ -1,0 +1,118 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+* libbsq.so loads and exports every function include/bsq.h declares;
+* argument validation returns the documented status before any launch;
+* the library's host packer (an independent C++ implementation) is
+  byte-identical to the oracle's pack on every workload shape.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from block_scaled_bit_e2m1_amd import bsq, workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "bsq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsq_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_header_function():
+    L = bsq.lib()
+    names = header_functions()
+    assert len(names) >= 9
+    for name in names:
+        assert hasattr(L, name), name
+    assert set(names) == set(bsq.EXPORTS)
+    assert bsq.bsq_version().startswith("bsq")
+
+
+def test_status_strings():
+    for s in range(7):
+        assert bsq.bsq_status_string(s)
+    assert bsq.bsq_status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("fmt,n,k,want", [
+    ("mxfp4", 16, 512, (4096, 256, 0)),
+    ("nvfp4", 4096, 4096, (8 << 20, 1 << 20, 0)),
+    ("mxfp8_e4m3", 14336, 4096, (56 << 20, 14336 * 128, 0)),
+    ("int4_affine", 11008, 4096, (11008 * 2048, 11008 * 128, 11008 * 128)),
+    ("int8_sym", 11008, 4096, (11008 * 4096, 11008 * 512, 0)),
+    ("nvfp8", 8, 48, (384, 8 * 3 * 4, 0)),
+])
+def test_packed_bytes(fmt, n, k, want, orc):
+    assert bsq.packed_bytes(fmt, n, k) == want
+    assert orc.sizes(fmt, n, k) == want
+
+
+def test_validation_errors():
+    null = None
+    st, *_ = bsq.bsq_packed_bytes(99, 0, 4, 32)
+    assert st == bsq.ERR_UNSUPPORTED
+    st, *_ = bsq.bsq_packed_bytes(bsq.MXFP4, 16, 4, 32)
+    assert st == bsq.ERR_UNSUPPORTED  # wrong block
+    st, *_ = bsq.bsq_packed_bytes(bsq.MXFP4, 0, 4, 48)
+    assert st == bsq.ERR_SHAPE
+    st, *_ = bsq.bsq_packed_bytes(bsq.NVFP4, 0, -1, 32)
+    assert st == bsq.ERR_ARG
+    # matmul argument checks happen before any device call
+    p = ctypes.c_void_p(16)
+    assert bsq.bsq_qgemm(bsq.MXFP4, 0, 2, 4, 48, p, p, null, 1.0, p, bsq.BF16, p, bsq.BF16, null) == bsq.ERR_SHAPE
+    assert bsq.bsq_qgemm(bsq.MXFP4, 0, 2, 4, 64, p, p, null, 1.0, p, 7, p, bsq.BF16, null) == bsq.ERR_ARG
+    assert bsq.bsq_qgemm(bsq.MXFP4, 0, 2, 4, 64, None, p, null, 1.0, p, bsq.BF16, p, bsq.BF16, null) == bsq.ERR_ARG
+    assert bsq.bsq_qgemm(bsq.INT4_AFFINE, 0, 2, 4, 64, p, p, null, 1.0, p, bsq.BF16, p, bsq.BF16, null) == bsq.ERR_ARG
+    mis = ctypes.c_void_p(8)
+    assert bsq.bsq_qgemm(bsq.MXFP4, 0, 2, 4, 64, mis, p, null, 1.0, p, bsq.BF16, p, bsq.BF16, null) == bsq.ERR_ALIGN
+    assert bsq.bsq_qgemm(bsq.MXFP4, 0, 2, 4, 64, p, p, null, 1.0, mis, bsq.BF16, p, bsq.BF16, null) == bsq.ERR_ALIGN
+    assert bsq.bsq_qgemm(bsq.MXFP4, 0, 2, 4, 64, p, p, null, 1.0, p, bsq.BF16, ctypes.c_void_p(17), bsq.BF16,
+                         null) == bsq.ERR_ALIGN
+    assert bsq.bsq_qgemm_path(bsq.PATH_MFMA, bsq.MXFP4, 0, 2, 4, 64, p, p, null, 1.0, p, bsq.F32, p, bsq.F32,
+                              null) == bsq.ERR_UNSUPPORTED
+    assert bsq.bsq_qgemm_path(9, bsq.MXFP4, 0, 2, 4, 64, p, p, null, 1.0, p, bsq.BF16, p, bsq.BF16, null) == bsq.ERR_ARG
+    assert bsq.bsq_dequant(bsq.MXFP4, 0, 4, 64, p, p, null, 1.0, ctypes.c_void_p(20), null) == bsq.ERR_ALIGN
+    # empty shapes are accepted and launch nothing
+    assert bsq.bsq_qgemm(bsq.MXFP4, 0, 0, 4, 64, None, None, null, 1.0, None, bsq.BF16, None, bsq.BF16, null) == bsq.OK
+    assert bsq.bsq_qgemv(bsq.MXFP4, 0, 0, 64, None, None, null, 1.0, None, bsq.BF16, None, bsq.BF16, null) == bsq.OK
+    assert bsq.bsq_dequant(bsq.MXFP4, 0, 0, 64, None, None, null, 1.0, None, null) == bsq.OK
+    assert "aligned" in bsq.bsq_last_error() or bsq.bsq_last_error() == ""
+
+
+def test_pack_rejects_nonfinite():
+    w = np.zeros((2, 32), np.float32)
+    w[1, 1] = np.nan
+    with pytest.raises(bsq.BsqError) as e:
+        bsq.pack("mxfp4", w)
+    assert e.value.status == bsq.ERR_NONFINITE
+
+
+def _same_pack(p, q):
+    return ((p["codes"] == q.codes.numpy()).all() and (p["scales"] == q.scales.numpy()).all()
+            and (p["biases"] is None or (p["biases"] == q.biases.numpy()).all()) and p["global"] == q.global_scale)
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_library_pack_equals_oracle_pack(orc, name):
+    wl = workloads.WORKLOADS[name]
+    n = min(wl.n, 2048)  # full k, first rows of the workload's recipe
+    W, _ = workloads.generate(wl, m=1, n=n)
+    assert _same_pack(orc.pack(wl.fmt, W), bsq.pack(wl.fmt, W))
+
+
+@pytest.mark.parametrize("fmt", list(bsq.FORMATS))
+def test_library_pack_equals_oracle_pack_edge_values(orc, fmt):
+    rng = np.random.default_rng(77)
+    w = (rng.standard_normal((40, 256)) * np.exp(rng.uniform(-30, 30, (40, 1)))).astype(np.float32)
+    w[0] = 0
+    w[1, :64] = -0.0
+    w[2] = np.float32(3.4e38) * np.sign(rng.standard_normal(256)).astype(np.float32)
+    w[3] = np.float32(1e-45)
+    w[4, ::2] = 6.0
+    w[5] = np.linspace(-7, 7, 256, dtype=np.float32)
+    assert _same_pack(orc.pack(fmt, w), bsq.pack(fmt, w))

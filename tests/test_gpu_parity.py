@@ -1,0 +1,276 @@
+"""GPU parity: the HIP path (through the C ABI) against the oracle.
+
+Bar (from the method's statement of correctness):
+  * dequant: bit-exact, NaN matching NaN and -0 kept;
+  * matmul: |gpu - ref| <= tol * sum_p |x_p * w_p| per output, tol = 2e-3 for
+    bf16 X / output with fp32 accumulation, 1e-5 for f32 X / output;
+  * the library's pack is byte-identical to the oracle's (checked on the CPU).
+
+Small cases span several tiles and ragged tails in m, n and k; the workload
+sizes run in the launch configuration the benchmark times, against the full
+oracle (decode GEMVs) or a seeded sample of rows (prefill GEMMs).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_scaled_bit_e2m1_amd import bsq, workloads
+
+pytestmark = pytest.mark.gpu
+
+ALL = list(bsq.FORMATS)
+BLOCK = {"mxfp4": 32, "nvfp4": 16, "mxfp8_e4m3": 32, "mxfp8_e5m2": 32, "nvfp8": 16, "int4_affine": 64, "int8_sym": 32}
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    bsq.lib()
+    oracle.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def same_bits(a, b):
+    a = np.ascontiguousarray(a, np.float32)
+    b = np.ascontiguousarray(b, np.float32)
+    both_nan = np.isnan(a) & np.isnan(b)
+    return (a.view(np.uint32) == b.view(np.uint32)) | both_nan
+
+
+def check_bound(out, ref, den, tol, what):
+    out = np.asarray(out, np.float64)
+    ok = np.abs(out - ref) <= tol * den
+    if not ok.all():
+        idx = np.argwhere(~ok)[:5]
+        msg = "; ".join(f"{tuple(i)}: gpu={out[tuple(i)]!r} ref={ref[tuple(i)]!r} den={den[tuple(i)]!r}" for i in idx)
+        raise AssertionError(f"{what}: {int((~ok).sum())} of {ok.size} outside {tol}*sum|x*w|; {msg}")
+
+
+def packed(fmt, W):
+    p = oracle.pack(fmt, W)
+    pw = bsq.PackedWeight(p["fmt"], p["n"], p["k"], torch.from_numpy(p["codes"]), torch.from_numpy(p["scales"]),
+                          None if p["biases"] is None else torch.from_numpy(p["biases"]), p["global"])
+    return p, bsq.to_device(pw, DEV)
+
+
+def raw_weight(fmt, n, k, codes, scales, biases=None, g=1.0):
+    p = {"fmt": oracle.FORMATS[fmt], "n": n, "k": k, "codes": np.ascontiguousarray(codes, np.uint8),
+         "scales": np.ascontiguousarray(scales).view(np.uint8).reshape(-1),
+         "biases": None if biases is None else np.ascontiguousarray(biases).view(np.uint8).reshape(-1),
+         "global": float(np.float32(g))}
+    pw = bsq.PackedWeight(p["fmt"], n, k, torch.from_numpy(p["codes"]), torch.from_numpy(p["scales"]),
+                          None if p["biases"] is None else torch.from_numpy(p["biases"]), p["global"])
+    return p, bsq.to_device(pw, DEV)
+
+
+# ----------------------------------------------------------------- dequant
+@pytest.mark.parametrize("fmt", ALL)
+@pytest.mark.parametrize("shape", [(16, 512), (37, 192)])
+def test_dequant_bit_exact_packed(fmt, shape):
+    n, k = shape
+    W = workloads.random_weights(n, k, seed=1000 + n, sigma=1.0, outliers=True)
+    p, d = packed(fmt, W)
+    got = bsq.dequant(d).cpu().numpy()
+    assert same_bits(got, oracle.dequant_packed(p)).all()
+
+
+def test_dequant_config1_all_8192_codes():
+    wl = workloads.WORKLOADS["mxfp4_m8_n16_k512"]
+    W, _ = workloads.generate(wl)
+    p, d = packed("mxfp4", W)
+    got = bsq.dequant(d).cpu().numpy()
+    assert got.size == 8192
+    assert same_bits(got, oracle.dequant_packed(p)).all()
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8_e4m3", "mxfp8_e5m2"])
+def test_dequant_exhaustive_codes_x_all_e8m0(fmt):
+    ncode = 16 if fmt == "mxfp4" else 256
+    n, k = 256, (256 if fmt == "mxfp4" else 8192)
+    codes = np.tile(np.arange(ncode), (n, k // ncode))
+    raw = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8) if fmt == "mxfp4" else codes.astype(np.uint8)
+    scales = np.repeat(np.arange(256, dtype=np.uint8), k // 32)
+    p, d = raw_weight(fmt, n, k, raw.reshape(-1), scales)
+    got = bsq.dequant(d).cpu().numpy()
+    want = oracle.dequant_packed(p)
+    assert same_bits(got, want).all()
+    assert np.signbit(got[:255, 8 if fmt == "mxfp4" else 0x80]).all()  # -0 stays -0
+
+
+def test_dequant_exhaustive_nvfp4_micro_scales():
+    n, k = 256, 256
+    codes = np.tile(np.arange(16), (n, k // 16))
+    raw = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8).reshape(-1)
+    scales = np.repeat(np.arange(256, dtype=np.uint8), k // 16)
+    for g in [1.0, 7.44e-6, 0.0014506777, 3.0e30, 1e-40]:
+        p, d = raw_weight("nvfp4", n, k, raw, scales, g=g)
+        assert same_bits(bsq.dequant(d).cpu().numpy(), oracle.dequant_packed(p)).all(), g
+
+
+def test_dequant_integer_and_f32_scale_sweeps():
+    rng = np.random.default_rng(5)
+    n, k = 64, 256
+    raw8 = np.tile(np.arange(256, dtype=np.uint8), n * k // 256)
+    s32 = (rng.standard_normal(n * k // 32) * np.exp(rng.uniform(-60, 60, n * k // 32))).astype(np.float32)
+    p, d = raw_weight("int8_sym", n, k, raw8, s32)
+    assert same_bits(bsq.dequant(d).cpu().numpy(), oracle.dequant_packed(p)).all()
+    s16 = (rng.standard_normal(n * k // 16) * np.exp(rng.uniform(-60, 60, n * k // 16))).astype(np.float32)
+    p, d = raw_weight("nvfp8", n, k, raw8, s16)
+    assert same_bits(bsq.dequant(d).cpu().numpy(), oracle.dequant_packed(p)).all()
+    raw4 = np.tile(np.arange(256, dtype=np.uint8), n * k // 2 // 256)
+    sb = torch.from_numpy((rng.standard_normal(n * k // 64) * 1e-2).astype(np.float32)).to(torch.bfloat16)
+    bb = torch.from_numpy((rng.standard_normal(n * k // 64) * 1e-1).astype(np.float32)).to(torch.bfloat16)
+    p, d = raw_weight("int4_affine", n, k, raw4, sb.view(torch.uint16).numpy(), bb.view(torch.uint16).numpy())
+    assert same_bits(bsq.dequant(d).cpu().numpy(), oracle.dequant_packed(p)).all()
+
+
+# ----------------------------------------------------------------- matmul
+def run_matmul(fmt, m, n, k, act, path, seed=0, sigma=0.02, outliers=True, out_dtype=None):
+    W = workloads.random_weights(n, k, seed=seed + 17, sigma=sigma, outliers=outliers)
+    X = workloads.random_activations(m, k, seed=seed + 29, act=act)
+    p, d = packed(fmt, W)
+    wd = oracle.dequant_packed(p)
+    ref, den = oracle.matmul(X, wd)
+    xt = torch.from_numpy(X).to(torch.bfloat16 if act == "bf16" else torch.float32).to(DEV)
+    od = out_dtype or xt.dtype
+    if path == "gemv":
+        out = bsq.qgemv(d, xt[0], out_dtype=od)[None, :]
+    else:
+        out = bsq.qgemm(d, xt, out_dtype=od, path=path)
+    return out.float().cpu().numpy(), ref, den
+
+
+@pytest.mark.parametrize("fmt", ALL)
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+def test_qgemv_parity(fmt, act):
+    for n, k in [(300, 1024), (5, 64 * 3), (129, 4096)]:
+        if k % BLOCK[fmt]:
+            continue
+        out, ref, den = run_matmul(fmt, 1, n, k, act, "gemv", seed=n + k)
+        check_bound(out, ref, den, 2e-3 if act == "bf16" else 1e-5, f"qgemv {fmt} {act} n={n} k={k}")
+
+
+def test_qgemv_nvfp4_k_not_multiple_of_32():
+    out, ref, den = run_matmul("nvfp4", 1, 77, 16 * 21, "bf16", "gemv", seed=3)
+    check_bound(out, ref, den, 2e-3, "qgemv nvfp4 k=336")
+    out, ref, den = run_matmul("nvfp4", 5, 77, 16 * 21, "bf16", bsq.PATH_MFMA, seed=4)
+    check_bound(out, ref, den, 2e-3, "mfma nvfp4 k=336")
+
+
+@pytest.mark.parametrize("fmt", ALL)
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+def test_qgemm_rows_parity(fmt, act):
+    for m in [2, 3, 8, 13]:
+        out, ref, den = run_matmul(fmt, m, 70, 512, act, bsq.PATH_ROWS, seed=m)
+        check_bound(out, ref, den, 2e-3 if act == "bf16" else 1e-5, f"rows {fmt} {act} m={m}")
+
+
+@pytest.mark.parametrize("fmt", ALL)
+def test_qgemm_mfma_parity(fmt):
+    for m, n, k in [(1, 72, 256), (40, 300, 1024), (200, 130, 192), (257, 129, 64 * 5 + (32 if BLOCK[fmt] <= 32 else 0))]:
+        if k % BLOCK[fmt]:
+            continue
+        out, ref, den = run_matmul(fmt, m, n, k, "bf16", bsq.PATH_MFMA, seed=m * 7 + n)
+        check_bound(out, ref, den, 2e-3, f"mfma {fmt} m={m} n={n} k={k}")
+
+
+@pytest.mark.parametrize("fmt", ALL)
+def test_mfma_f32_output(fmt):
+    out, ref, den = run_matmul(fmt, 64, 96, 256, "bf16", bsq.PATH_MFMA, seed=11, out_dtype=torch.float32)
+    check_bound(out, ref, den, 2e-3, f"mfma f32-out {fmt}")
+
+
+@pytest.mark.parametrize("fmt", ALL)
+def test_qgemv_equals_qgemm_m1_paths(fmt):
+    """m=1 through qgemv, the streaming qgemm and the MFMA qgemm agree."""
+    n, k = 200, 1024
+    W = workloads.random_weights(n, k, seed=5, sigma=0.02)
+    X = workloads.random_activations(1, k, seed=6)
+    p, d = packed(fmt, W)
+    ref, den = oracle.matmul(X, oracle.dequant_packed(p))
+    xt = torch.from_numpy(X).to(torch.bfloat16).to(DEV)
+    a = bsq.qgemv(d, xt[0], out_dtype=torch.float32).cpu().numpy()[None]
+    b = bsq.qgemm(d, xt, out_dtype=torch.float32, path=bsq.PATH_ROWS).cpu().numpy()
+    c = bsq.qgemm(d, xt, out_dtype=torch.float32, path=bsq.PATH_MFMA).cpu().numpy()
+    assert (a == b).all()  # same kernel family, same order
+    for o, name in [(a, "qgemv"), (c, "mfma")]:
+        check_bound(o, ref, den, 2e-3, f"{name} {fmt}")
+    check_bound(c, a.astype(np.float64), den, 4e-3, f"mfma vs qgemv {fmt}")
+
+
+def test_k_zero_gives_zeros_and_empty_shapes():
+    d = bsq.PackedWeight(bsq.MXFP4, 5, 0, torch.zeros(16, dtype=torch.uint8, device=DEV),
+                         torch.zeros(1, dtype=torch.uint8, device=DEV), None, 1.0)
+    x = torch.zeros((3, 0), dtype=torch.bfloat16, device=DEV)
+    out = torch.full((3, 5), 7.0, dtype=torch.bfloat16, device=DEV)
+    bsq.qgemm(d, x, out=out)
+    assert (out.float().cpu() == 0).all()
+    out2 = torch.full((0, 5), 7.0, dtype=torch.bfloat16, device=DEV)
+    bsq.qgemm(d, torch.zeros((0, 0), dtype=torch.bfloat16, device=DEV), out=out2)
+
+
+@pytest.mark.parametrize("path", [bsq.PATH_ROWS, bsq.PATH_MFMA])
+def test_nan_scale_and_code_propagate(path):
+    n, k, m = 64, 128, 4
+    W = workloads.random_weights(n, k, seed=8, sigma=0.02)
+    p = oracle.pack("mxfp8_e4m3", W)
+    p["scales"] = p["scales"].copy()
+    p["codes"] = p["codes"].copy()
+    p["scales"][3 * (k // 32) + 1] = 255  # NaN scale in row 3
+    p["codes"][10 * k + 5] = 0x7F  # NaN code in row 10
+    pw = bsq.to_device(bsq.PackedWeight(p["fmt"], n, k, torch.from_numpy(p["codes"]), torch.from_numpy(p["scales"]),
+                                        None, 1.0), DEV)
+    X = workloads.random_activations(m, k, seed=9)
+    out = bsq.qgemm(pw, torch.from_numpy(X).to(torch.bfloat16).to(DEV), out_dtype=torch.float32, path=path).cpu().numpy()
+    assert np.isnan(out[:, 3]).all() and np.isnan(out[:, 10]).all()
+    assert np.isfinite(np.delete(out, [3, 10], axis=1)).all()
+
+
+# ----------------------------------------------------------------- workloads
+def _workload_case(name, sample_rows=None):
+    wl = workloads.WORKLOADS[name]
+    W, X = workloads.generate(wl)
+    pw = bsq.to_device(bsq.pack(wl.fmt, W), DEV)
+    p = oracle.pack(wl.fmt, W)
+    assert (p["codes"] == pw.codes.cpu().numpy()).all()
+    wd = oracle.dequant_packed(p)
+    xt = torch.from_numpy(X).to(torch.bfloat16 if wl.act == "bf16" else torch.float32).to(DEV)
+    if wl.op == "qgemv":
+        out = bsq.qgemv(pw, xt[0])[None, :]
+    else:
+        out = bsq.qgemm(pw, xt)
+    out = out.float().cpu().numpy()
+    rows = None
+    if sample_rows:
+        rng = np.random.default_rng(wl.seed + 7)
+        rows = np.unique(np.concatenate([[0, wl.m - 1], rng.choice(wl.m, sample_rows, replace=False)]))
+        out = out[rows]
+    ref, den = oracle.matmul(X, wd, rows=rows)
+    check_bound(out, ref, den, wl.tol, name)
+    assert np.isfinite(out).all()
+
+
+def test_workload_mxfp4_m8_f32():
+    _workload_case("mxfp4_m8_n16_k512")
+
+
+def test_workload_nvfp4_qgemv_4096():
+    _workload_case("nvfp4_qgemv_4096")
+
+
+@pytest.mark.parametrize("name", ["mxfp8_e4m3_qgemv_14336", "mxfp8_e5m2_qgemv_14336"])
+def test_workload_mxfp8_qgemv_14336(name):
+    _workload_case(name)
+
+
+def test_workload_mxfp4_qgemm_2048_sampled():
+    _workload_case("mxfp4_qgemm_2048", sample_rows=96)
+
+
+@pytest.mark.parametrize("name", ["int4_affine_qgemm_512", "int8_sym_qgemm_512"])
+def test_workload_c5_sampled(name):
+    _workload_case(name, sample_rows=48)
