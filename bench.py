@@ -1,0 +1,265 @@
+"""Benchmark: block-scaled decode GEMV (and prefill GEMM) on one MI355X.
+
+Default workload (one step = one launch of the fused qgemv kernel: weight
+stream, decode, block-scale fold and dot, A1-A4 of the hot path):
+    nvfp4 decode GEMV, m=1, n=k=4096, W ~ N(0, 0.02) packed to E2M1 codes +
+    E4M3 micro-scales per 16 + f32 global, x bf16 ~ N(0,1), out bf16.
+
+`value` is the weight-stream rate (codes + scales + global bytes per launch
+divided by the time per launch) with every input already resident in HBM.
+Launches rotate over enough distinct copies of the packed weight (> 512 MB)
+that each launch reads its weight from HBM, not from the 256 MB Infinity
+Cache; launches are replayed from a HIP graph so host launch cost is not
+measured.  The same line carries the prefill GEMM (mxfp4, m=2048, n=k=4096)
+and the other decode/prefill workloads as `extra` entries, a `roofline` object
+for the timed kernel, and the CPU oracle timed on a bounded sample as
+`cpu_baseline`.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-extra] [--no-cpu] [--only-timed]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
+ROTATE_BYTES = 640 << 20        # distinct weight copies per rotation (> 2x the 256 MB MALL)
+
+KERNEL_SOURCES = {"qgemv": "block_scaled_bit_e2m1_amd/csrc/rows.hip",
+                  "qgemm": "block_scaled_bit_e2m1_amd/csrc/mfma.hip"}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_sha(kind):
+    h = hashlib.sha256()
+    for rel in [KERNEL_SOURCES[kind], "block_scaled_bit_e2m1_amd/csrc/codec.hpp"]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kind):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    e = t.get(workload)
+    if not e or e.get("source_sha") != source_sha(kind):
+        return None
+    return e.get("bytes_per_launch")
+
+
+def setup(wl, device, rotate=True):
+    import torch
+
+    from block_scaled_bit_e2m1_amd import bsq, workloads
+
+    W, X = workloads.generate(wl)
+    pw = bsq.pack(wl.fmt, W)
+    wbytes = pw.weight_bytes + (4 if wl.fmt == "nvfp4" else 0)
+    copies = max(1, ROTATE_BYTES // max(1, pw.weight_bytes)) if (rotate and wl.op == "qgemv") else 1
+    dev = [bsq.to_device(pw, device) for _ in range(copies)]
+    xdt = torch.bfloat16 if wl.act == "bf16" else torch.float32
+    x = torch.from_numpy(X).to(xdt).to(device)
+    if wl.op == "qgemv":
+        x = x[0]
+        out = torch.empty((wl.n,), dtype=xdt, device=device)
+    else:
+        out = torch.empty((wl.m, wl.n), dtype=xdt, device=device)
+    return {"W": W, "X": X, "pw": pw, "dev": dev, "x": x, "out": out, "wbytes": wbytes, "copies": copies}
+
+
+def launch(wl, d, i):
+    from block_scaled_bit_e2m1_amd import bsq
+
+    w = d["dev"][i % len(d["dev"])]
+    if wl.op == "qgemv":
+        bsq.qgemv(w, d["x"], out=d["out"])
+    else:
+        bsq.qgemm(w, d["x"], out=d["out"])
+
+
+def time_workload(wl, steps, warmup, device, rotate=True):
+    """Per-launch time (ms) over `steps` launches replayed from HIP graphs,
+    measured with events on the launch stream and with the host clock."""
+    import torch
+
+    d = setup(wl, device, rotate)
+    per_graph = d["copies"] if wl.op == "qgemv" else 1
+    per_graph = max(1, min(per_graph, steps))
+    stream = torch.cuda.Stream(device)
+    torch.cuda.synchronize(device)
+    with torch.cuda.stream(stream):
+        for i in range(per_graph):  # eager warm-up of every copy before capture
+            launch(wl, d, i)
+    torch.cuda.synchronize(device)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(per_graph):
+            launch(wl, d, i)
+    reps = max(1, steps // per_graph)
+    wreps = max(1, warmup // per_graph) if warmup > 0 else 0
+    with torch.cuda.stream(stream):
+        for _ in range(wreps):
+            g.replay()
+    torch.cuda.synchronize(device)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize(device)
+    t1 = time.perf_counter()
+    launches = reps * per_graph
+    ev_ms = e0.elapsed_time(e1) / launches
+    wall_ms = (t1 - t0) * 1e3 / launches
+    return {"launches": launches, "event_ms": ev_ms, "wall_ms": wall_ms, "wbytes": d["wbytes"], "copies": d["copies"],
+            "data": d}
+
+
+def hot_time(wl, device, iters=200):
+    """Same launch on one resident copy (served partly from the Infinity Cache)."""
+    r = time_workload(wl, iters, 20, device, rotate=False)
+    return r["event_ms"]
+
+
+def cpu_baseline(wl, budget_s=10.0):
+    """The oracle as it stands (dequant, then fp64 dot) on the host cores."""
+    import numpy as np
+
+    import oracle
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+    W, X = __import__("block_scaled_bit_e2m1_amd.workloads", fromlist=["generate"]).generate(wl)
+    p = oracle.pack(wl.fmt, W)
+    wb = p["codes"].size + p["scales"].size + (0 if p["biases"] is None else p["biases"].size)
+    wb += 4 if wl.fmt == "nvfp4" else 0
+    reps, t_total = 0, 0.0
+    if wl.op == "qgemv":
+        while t_total < budget_s or reps < 2:
+            t0 = time.perf_counter()
+            wd = oracle.dequant_packed(p)
+            oracle.matmul(X, wd, threads=threads)
+            t_total += time.perf_counter() - t0
+            reps += 1
+        v = wb * reps / t_total / 1e9
+        return {"value": round(v, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+                "sample": f"{reps} full passes of {wl.name} (dequant to f32 on 1 core, then fp64 dot on "
+                          f"{threads} threads), {t_total:.1f} s"}
+    rows = max(1, min(wl.m, 16))
+    t0 = time.perf_counter()
+    wd = oracle.dequant_packed(p)
+    oracle.matmul(X, wd, rows=np.arange(rows), threads=threads)
+    t = time.perf_counter() - t0
+    v = 2.0 * rows * wl.n * wl.k / t / 1e12
+    return {"value": round(v, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"dequant + fp64 dot of {rows} of {wl.m} rows of {wl.name}, {t:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3000)
+    ap.add_argument("--warmup", type=int, default=300)
+    ap.add_argument("--workload", default="nvfp4_qgemv_4096")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only-timed", action="store_true", help="timed workload only (for profiling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (this build has no multi-GPU "
+              f"path; the decode/prefill kernels shard along n with no exchange step).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from block_scaled_bit_e2m1_amd import bsq, workloads
+
+    device = torch.device("cuda:0")
+    bsq.lib()
+    wl = workloads.WORKLOADS[args.workload]
+    kind = "qgemv" if wl.op == "qgemv" else "qgemm"
+    log(f"bench: {wl.name} steps={args.steps} warmup={args.warmup}")
+    r = time_workload(wl, args.steps, args.warmup, device)
+    ms = r["wall_ms"]
+    if kind == "qgemv":
+        metric, unit = "weight-stream GB/s (qgemv m=1)", "GB/s"
+        value = r["wbytes"] / (ms * 1e-3) / 1e9
+        io_bytes = 2 * (wl.k + wl.n) if wl.act == "bf16" else 4 * (wl.k + wl.n)
+        alg = r["wbytes"] + io_bytes
+        achieved = alg / (r["event_ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name, kind),
+                "kernel": "rows_kernel (bsq_qgemv)", "alg_bytes_per_launch": alg,
+                "event_ms_per_launch": round(r["event_ms"], 6)}
+    else:
+        metric, unit = "TFLOP/s (qgemm)", "TFLOP/s"
+        value = wl.flops / (ms * 1e-3) / 1e12
+        achieved = wl.flops / (r["event_ms"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": measured_traffic(wl.name, kind),
+                "kernel": "mfma_kernel (bsq_qgemm)", "alg_flops_per_launch": wl.flops,
+                "event_ms_per_launch": round(r["event_ms"], 6)}
+    log(f"  {wl.name}: {value:.1f} {unit}  ({r['event_ms'] * 1e3:.2f} us/launch by events, "
+        f"{ms * 1e3:.2f} us by host clock, {r['copies']} weight copies)")
+
+    extra = []
+    if not args.no_extra and not args.only_timed:
+        hot = hot_time(wl, device)
+        extra.append({"workload": wl.name, "note": "same launch on one resident weight copy (Infinity Cache hot)",
+                      "us_per_launch": round(hot * 1e3, 3), "value": round(r["wbytes"] / (hot * 1e-3) / 1e9, 2)
+                      if kind == "qgemv" else round(wl.flops / (hot * 1e-3) / 1e12, 2), "unit": unit})
+        for name, w2 in workloads.WORKLOADS.items():
+            if name == wl.name:
+                continue
+            steps = 400 if w2.op == "qgemm" and w2.m > 8 else 2000
+            r2 = time_workload(w2, steps, steps // 10, device)
+            if w2.op == "qgemv":
+                v, u = r2["wbytes"] / (r2["event_ms"] * 1e-3) / 1e9, "GB/s"
+                fr = v / HBM_PEAK_GBS
+            else:
+                v, u = w2.flops / (r2["event_ms"] * 1e-3) / 1e12, "TFLOP/s"
+                fr = v / MFMA_BF16_PEAK_TFLOPS if w2.act == "bf16" and w2.m > 8 else None
+            e = {"workload": name, "value": round(v, 3), "unit": u, "us_per_launch": round(r2["event_ms"] * 1e3, 3),
+                 "roofline_frac": None if fr is None else round(fr, 4)}
+            extra.append(e)
+            log(f"  {name}: {v:.2f} {u} ({r2['event_ms'] * 1e3:.2f} us/launch)")
+            del r2
+            torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu and not args.only_timed:
+        log("  cpu baseline (oracle) ...")
+        cpu = cpu_baseline(wl)
+
+    line = {
+        "metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": r["launches"],
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if wl.act == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,sigma) weights, N(0,1) activations)",
+        "config": {"workload": wl.name, "format": wl.fmt, "m": wl.m, "n": wl.n, "k": wl.k,
+                   "weight_copies_rotated": r["copies"], "graph_replay": True},
+        "roofline": roof, "cpu_baseline": cpu, "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
