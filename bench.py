@@ -94,13 +94,14 @@ def launch(wl, d, i):
         bsq.qgemm(w, d["x"], out=d["out"])
 
 
-def time_workload(wl, steps, warmup, device, rotate=True):
+def time_workload(wl, steps, warmup, device, rotate=True, per_graph=None):
     """Per-launch time (ms) over `steps` launches replayed from HIP graphs,
     measured with events on the launch stream and with the host clock."""
     import torch
 
     d = setup(wl, device, rotate)
-    per_graph = d["copies"] if wl.op == "qgemv" else 1
+    if per_graph is None:
+        per_graph = d["copies"] if wl.op == "qgemv" else 1
     per_graph = max(1, min(per_graph, steps))
     stream = torch.cuda.Stream(device)
     torch.cuda.synchronize(device)
@@ -136,7 +137,7 @@ def time_workload(wl, steps, warmup, device, rotate=True):
 
 def hot_time(wl, device, iters=200):
     """Same launch on one resident copy (served partly from the Infinity Cache)."""
-    r = time_workload(wl, iters, 20, device, rotate=False)
+    r = time_workload(wl, iters * 10, 50, device, rotate=False, per_graph=64)
     return r["event_ms"]
 
 

@@ -37,6 +37,8 @@
 #include "bsq_internal.hpp"
 #include "codec.hpp"
 
+#include <type_traits>
+
 namespace bsq {
 namespace {
 
@@ -208,7 +210,15 @@ __device__ __forceinline__ void decode_w(const WRaw &r, bf16x8_t hi[4], bf16x8_t
   }
 }
 
-template <int F, int BM, int BN, int WGM, int WGN, bool VEC>
+// Global data of one BK step held in registers: this thread's X chunks and
+// this lane's weight words for each of its NT column subtiles.
+template <int XCH, int NT>
+struct Slot {
+  uint4 x[XCH];
+  WRaw w[NT];
+};
+
+template <int F, int BM, int BN, int WGM, int WGN, int D, int UK, bool VEC, bool ROT, int SCHED>
 __global__ void __launch_bounds__(WGM *WGN * 64)
 mfma_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, const uint16_t *__restrict__ biases,
             float global, const uint16_t *__restrict__ x, void *__restrict__ out, int ot, int64_t m, int64_t n,
@@ -231,16 +241,13 @@ mfma_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
   const int wm = wid / WGN, wn = wid - (wid / WGN) * WGN;
   const int l32 = lane & 31, h = lane >> 5;
 
-  // X chunk c of this thread: row c / 8, 8-element column group c % 8.
-  int64_t xrow[XCH];
-  int xcol[XCH];
+  // X chunk c of this thread: tile row cid / 8, 8-element column group cid % 8.
+  const uint16_t *xp[XCH];
 #pragma unroll
   for (int c = 0; c < XCH; ++c) {
     const int cid = c * NTHR + tid;
-    const int r = cid >> 3;
-    int64_t gr = m0 + r;
-    xrow[c] = gr < m ? gr : m - 1;  // rows past m read a valid row; never stored
-    xcol[c] = (cid & 7) * 8;
+    const int64_t gr = m0 + (cid >> 3);
+    xp[c] = x + (gr < m ? gr : m - 1) * k + (cid & 7) * 8;  // rows past m read a valid row; never stored
   }
   int64_t wcol[NT];
 #pragma unroll
@@ -257,66 +264,146 @@ mfma_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  const int KT = (int)((k + BK - 1) / BK);
-  uint4 xr[XCH];
-  WRaw wr[NT];
+  const int KT = (int)((k + BK - 1) / BK);  // k steps, the last one possibly ragged
+  const int KF = (int)(k / BK);              // full k steps
+  // Rotation of the k walk: the workgroups that run together on one XCD start
+  // at different k steps, so their concurrent requests spread over the L2
+  // channels instead of all hitting the same rows' lines at once.  Only when
+  // every step is full (the sum is order-free up to fp32 rounding).
+  int krot = 0;
+  if (ROT && KF == KT) krot = (int)(((int64_t)(blockIdx.x >> 3) * 7) % KT);
+  Slot<XCH, NT> G[D];
 
-  auto load_x = [&](int kt, bool tail) {
+  // Loads of step kt into a slot; GUARD handles the ragged last step.
+  auto load = [&](auto guard, Slot<XCH, NT> &g, int kt) {
+    constexpr bool kGuard = decltype(guard)::value;
+    if (ROT) {
+      kt += krot;
+      if (kt >= KT) kt -= KT;
+    }
     const int64_t k0 = (int64_t)kt * BK;
+    const bool tail = kGuard && kt >= KF;
 #pragma unroll
     for (int c = 0; c < XCH; ++c) {
-      const int64_t kk = k0 + xcol[c];
-      if (!tail || kk < k)
-        xr[c] = *reinterpret_cast<const uint4 *>(x + xrow[c] * k + kk);
+      if (!kGuard || !tail || k0 + ((c * NTHR + tid) & 7) * 8 < k)
+        g.x[c] = *reinterpret_cast<const uint4 *>(xp[c] + k0);
       else
-        xr[c] = make_uint4(0, 0, 0, 0);
+        g.x[c] = make_uint4(0, 0, 0, 0);
     }
+    const int64_t kb = k0 + 32 * h;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) load_w<F, VEC>(g.w[j], codes, scales, biases, wcol[j], k, kb, tail);
   };
-  auto store_x = [&](int buf) {
+  auto store_x = [&](const Slot<XCH, NT> &g, int buf) {
 #pragma unroll
     for (int c = 0; c < XCH; ++c) {
       const int cid = c * NTHR + tid;
-      *reinterpret_cast<uint4 *>(&xs[buf][(cid >> 3) * LDS_LD + (cid & 7) * 8]) = xr[c];
+      *reinterpret_cast<uint4 *>(&xs[buf][(cid >> 3) * LDS_LD + (cid & 7) * 8]) = g.x[c];
     }
   };
-  auto load_ws = [&](int kt, bool tail) {
-    const int64_t kb = (int64_t)kt * BK + 32 * h;
+  // One k step: decode this step's weights, refill the slot with step kt + D,
+  // multiply from LDS, stage step kt + 1 into the other LDS buffer.
+  auto read_a = [&](const uint16_t *xb, int s, bf16x8_t a[MT]) {
 #pragma unroll
-    for (int j = 0; j < NT; ++j) load_w<F, VEC>(wr[j], codes, scales, biases, wcol[j], k, kb, tail);
+    for (int i = 0; i < MT; ++i)
+      a[i] = *reinterpret_cast<const bf16x8_t *>(&xb[(wm * WTM + i * 32 + l32) * LDS_LD + 32 * h + 8 * s]);
   };
-
-  load_x(0, KT == 1);
-  load_ws(0, KT == 1);
-  store_x(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
+  auto mma = [&](const bf16x8_t a[MT], const bf16x8_t bh[NT], const bf16x8_t bl[NT]) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bh[j], acc[i][j], 0, 0, 0);
+        if constexpr (kSplit<F>) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bl[j], acc[i][j], 0, 0, 0);
+      }
+  };
+  auto step = [&](auto guard, int kt, Slot<XCH, NT> &cur, const Slot<XCH, NT> &nxt) {
+    constexpr bool kGuard = decltype(guard)::value;
+    const uint16_t *xb = xs[kt & 1];
     bf16x8_t bh[NT][4], bl[NT][4];
+    if constexpr (SCHED == 4) {
+      // Software-pipelined step in fenced phases: the MFMAs of slice s issue
+      // alongside the LDS reads of slice s+1, the weight decode, the global
+      // prefetch and (last) the LDS writes of the next step.
+      bf16x8_t a0[MT], a1[MT];
+      read_a(xb, 0, a0);
 #pragma unroll
-    for (int j = 0; j < NT; ++j) decode_w<F>(wr[j], bh[j], bl[j]);
-    const bool more = kt + 1 < KT;
-    if (more) {
-      const bool tail = kt + 2 == KT && (k % BK) != 0;
-      load_x(kt + 1, tail);
-      load_ws(kt + 1, tail);
-    }
-    const uint16_t *xb = xs[cur];
+      for (int j = 0; j < NT; ++j) decode_w<F>(cur.w[j], bh[j], bl[j]);
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8_t bs[NT], ls[NT];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-#pragma unroll
-      for (int i = 0; i < MT; ++i) {
-        const int row = wm * WTM + i * 32 + l32;
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(&xb[row * LDS_LD + 32 * h + 8 * s]);
+      for (int s = 0; s < 4; ++s) {
+        bf16x8_t *ac = (s & 1) ? a1 : a0;
+        bf16x8_t *an = (s & 1) ? a0 : a1;
+        if (s < 3) read_a(xb, s + 1, an);
+        if (s == 1) {
+          if (!kGuard || kt + D < KT) load(guard, cur, kt + D);
+        }
+        if (s == 3) {
+          if (!kGuard || kt + 1 < KT) store_x(nxt, (kt + 1) & 1);
+        }
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh[j][s], acc[i][j], 0, 0, 0);
-          if constexpr (kSplit<F>) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl[j][s], acc[i][j], 0, 0, 0);
+          bs[j] = bh[j][s];
+          ls[j] = bl[j][s];
         }
+        mma(ac, bs, ls);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      __syncthreads();
+      return;
     }
-    if (more) store_x(cur ^ 1);
+    bf16x8_t af[4][MT];
+    if constexpr (SCHED == 1) {
+      // All A fragments of the step first: their LDS latency overlaps the
+      // weight decode instead of stalling each MFMA pair.
+#pragma unroll
+      for (int s = 0; s < 4; ++s) read_a(xb, s, af[s]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) decode_w<F>(cur.w[j], bh[j], bl[j]);
+    if (!kGuard || kt + D < KT) load(guard, cur, kt + D);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if constexpr (SCHED != 1) read_a(xb, s, af[s]);
+      bf16x8_t bs[NT], ls[NT];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        bs[j] = bh[j][s];
+        ls[j] = bl[j][s];
+      }
+      mma(af[s], bs, ls);
+    }
+    if constexpr (SCHED == 2) __builtin_amdgcn_iglp_opt(0);
+    if constexpr (SCHED == 3) __builtin_amdgcn_iglp_opt(1);
+    if (!kGuard || kt + 1 < KT) store_x(nxt, (kt + 1) & 1);
     __syncthreads();
+  };
+  constexpr std::integral_constant<bool, false> kFast{};
+  constexpr std::integral_constant<bool, true> kGuarded{};
+
+  // Prologue: steps 0..D-1 in flight, step 0 staged in LDS.
+#pragma unroll
+  for (int s = 0; s < D; ++s)
+    if (s < KT) load(kGuarded, G[s], s);
+  store_x(G[0], 0);
+  __syncthreads();
+
+  // Steady state: every step and every prefetch is a full step, no guards.
+  // UK steps (a multiple of D) per trip: the compiler waits for all
+  // outstanding loads at the loop back-edge, so that happens once per UK steps.
+  static_assert(UK % D == 0, "UK must be a multiple of D");
+  int kt = 0;
+  for (; kt + UK + D <= KF; kt += UK) {
+#pragma unroll
+    for (int S = 0; S < UK; ++S) step(kFast, kt + S, G[S % D], G[(S + 1) % D]);
+  }
+  // Drain: the last steps, guarded.
+  for (; kt < KT; kt += D) {
+#pragma unroll
+    for (int S = 0; S < D; ++S)
+      if (kt + S < KT) step(kGuarded, kt + S, G[S], G[(S + 1) % D]);
   }
 
   // ---- epilogue ----
@@ -339,17 +426,17 @@ mfma_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
   }
 }
 
-template <int F, int BM, int BN, int WGM, int WGN>
+template <int F, int BM, int BN, int WGM, int WGN, int D, int UK, bool ROT = false, int SCHED = 1>
 hipError_t run_cfg(const QWeight &w, int64_t m, const void *x, void *out, int ot, hipStream_t s) {
   const int tiles_m = (int)((m + BM - 1) / BM), tiles_n = (int)((w.n + BN - 1) / BN);
   const dim3 grid((unsigned)(tiles_m * tiles_n));
   const bool vec = Traits<F>::kBits == 8 || (w.k % 32) == 0;
   if (vec)
-    hipLaunchKernelGGL((mfma_kernel<F, BM, BN, WGM, WGN, true>), grid, dim3(WGM * WGN * 64), 0, s,
+    hipLaunchKernelGGL((mfma_kernel<F, BM, BN, WGM, WGN, D, UK, true, ROT, SCHED>), grid, dim3(WGM * WGN * 64), 0, s,
                        (const uint8_t *)w.codes, w.scales, (const uint16_t *)w.biases, w.global, (const uint16_t *)x,
                        out, ot, m, w.n, w.k, tiles_m, tiles_n);
   else
-    hipLaunchKernelGGL((mfma_kernel<F, BM, BN, WGM, WGN, false>), grid, dim3(WGM * WGN * 64), 0, s,
+    hipLaunchKernelGGL((mfma_kernel<F, BM, BN, WGM, WGN, D, UK, false, ROT, SCHED>), grid, dim3(WGM * WGN * 64), 0, s,
                        (const uint8_t *)w.codes, w.scales, (const uint16_t *)w.biases, w.global, (const uint16_t *)x,
                        out, ot, m, w.n, w.k, tiles_m, tiles_n);
   return hipGetLastError();
@@ -358,10 +445,11 @@ hipError_t run_cfg(const QWeight &w, int64_t m, const void *x, void *out, int ot
 template <int F>
 hipError_t run_f(const QWeight &w, int64_t m, const void *x, void *out, int ot, hipStream_t s) {
   if ((m + 127) / 128 * ((w.n + 127) / 128) > (int64_t)1 << 30) return hipErrorInvalidValue;
-  // 256x128 tiles when they fill the chip, 128x128 otherwise.
+  // 256x128 tiles when they fill the 256 CUs, 128x128 otherwise.  Both use
+  // 2x2 waves, a two-deep register prefetch and the phased step schedule.
   const int64_t big = ((m + 255) / 256) * ((w.n + 127) / 128);
-  if (big >= 256) return run_cfg<F, 256, 128, 2, 2>(w, m, x, out, ot, s);
-  return run_cfg<F, 128, 128, 2, 2>(w, m, x, out, ot, s);
+  if (big >= 256) return run_cfg<F, 256, 128, 2, 2, 2, 4, false, 4>(w, m, x, out, ot, s);
+  return run_cfg<F, 128, 128, 2, 2, 2, 4, false, 4>(w, m, x, out, ot, s);
 }
 
 }  // namespace

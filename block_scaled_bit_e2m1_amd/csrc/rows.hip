@@ -7,10 +7,12 @@
 // with 16-byte loads and decoded in registers; every X row of the launch's
 // m-chunk reuses the decoded codes.
 //
-// Geometry (gfx950, wave64): a wave owns one weight row at a time.  Lane l
+// Geometry (gfx950, wave64): a wave owns RPW weight rows at a time.  Lane l
 // takes 16-byte code chunks l, l+64, l+128, ... along k (32 elements for 4-bit
-// codes, 16 for 8-bit).  Up to kUnroll chunks are loaded before any is used,
-// so a wave keeps several HBM requests in flight.  Per 8-element sub-chunk the
+// codes, 16 for 8-bit).  The code and scale loads of U chunks of all RPW rows
+// are issued before any is used, so a wave keeps RPW*U HBM requests in flight
+// and the whole weight of a decode GEMV is requested in one round.  Per
+// 8-element sub-chunk the
 // unscaled element values are dotted with X in fp32; the block scale is folded
 // once per block ("fold in that block's scale ONCE (not per element)" [rlx-cpu
 // quant.rs, dequant_matmul_int8]) and the nvfp4 global once at the end
@@ -107,20 +109,31 @@ __device__ __forceinline__ float dot8_f32(uint32_t w0, uint32_t w1, const float 
   return acc;
 }
 
-// Block scale of row j, block b as f32 (bias separately for int4).
+constexpr int kWaves = 4;  // waves per workgroup
+
+// Raw scale word of row j, block b (decoded after all loads are in flight).
 template <int F>
-__device__ __forceinline__ float load_scale(const void *scales, int64_t idx) {
-  if constexpr (F == kMXFP4 || F == kMXFP8_E4M3 || F == kMXFP8_E5M2)
-    return e8m0_to_f32(reinterpret_cast<const uint8_t *>(scales)[idx]);
-  else if constexpr (F == kNVFP4) return e4m3_to_f32(reinterpret_cast<const uint8_t *>(scales)[idx]);
-  else if constexpr (F == kNVFP8 || F == kINT8_SYM) return reinterpret_cast<const float *>(scales)[idx];
-  else return bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(scales)[idx]);
+__device__ __forceinline__ uint32_t load_scale_raw(const void *scales, int64_t idx) {
+  if constexpr (F == kMXFP4 || F == kMXFP8_E4M3 || F == kMXFP8_E5M2 || F == kNVFP4)
+    return reinterpret_cast<const uint8_t *>(scales)[idx];
+  else if constexpr (F == kNVFP8 || F == kINT8_SYM) return reinterpret_cast<const uint32_t *>(scales)[idx];
+  else return reinterpret_cast<const uint16_t *>(scales)[idx];
 }
 
-constexpr int kWaves = 4;   // waves per workgroup
-constexpr int kUnroll = 4;  // 16-byte code chunks loaded per lane before use
+template <int F>
+__device__ __forceinline__ float scale_value(uint32_t raw) {
+  if constexpr (F == kMXFP4 || F == kMXFP8_E4M3 || F == kMXFP8_E5M2) return e8m0_to_f32(raw);
+  else if constexpr (F == kNVFP4) return e4m3_to_f32(raw);
+  else if constexpr (F == kNVFP8 || F == kINT8_SYM) return __uint_as_float(raw);
+  else return bf16_bits_to_f32(raw);
+}
 
-template <int F, int M, int XT, bool VEC>
+// A wave owns RPW consecutive weight rows.  Per round it issues the 16-byte
+// code loads (U chunks per row) and the scale loads of all RPW rows before
+// any arithmetic, so every HBM request of the round is in flight at once;
+// X (resident in L2) is loaded per 8-element sub-chunk and shared by the RPW
+// rows.
+template <int F, int M, int XT, bool VEC, int RPW, int U>
 __global__ void __launch_bounds__(kWaves * 64)
 rows_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, const uint16_t *__restrict__ biases,
             float global, const void *__restrict__ xv, void *__restrict__ out, int ot, int64_t m, int64_t n, int64_t k) {
@@ -136,56 +149,75 @@ rows_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
   const int64_t nblk = k / B;
   const int64_t row_bytes = Traits<F>::kBits == 4 ? k / 2 : k;
 
-  for (int64_t j = wave; j < n; j += nwaves) {
-    float acc[M];
+  for (int64_t j0 = wave * RPW; j0 < n; j0 += nwaves * RPW) {
+    float acc[RPW][M];
 #pragma unroll
-    for (int mi = 0; mi < M; ++mi) acc[mi] = 0.0f;
-    const uint8_t *crow = codes + j * row_bytes;
+    for (int r = 0; r < RPW; ++r)
+#pragma unroll
+      for (int mi = 0; mi < M; ++mi) acc[r][mi] = 0.0f;
 
-    for (int64_t kc0 = (int64_t)lane * E; kc0 < k; kc0 += (int64_t)64 * E * kUnroll) {
-      uint4 cw[kUnroll];
+    for (int64_t kc0 = (int64_t)lane * E; kc0 < k; kc0 += (int64_t)64 * E * U) {
+      // ---- phase A: every HBM load of the round ----
+      uint4 cw[RPW][U];
+      uint32_t sr[RPW][U][NB], br[RPW][U];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int64_t kc = kc0 + (int64_t)u * 64 * E;
-        const int64_t off = Traits<F>::kBits == 4 ? kc / 2 : kc;
-        if (VEC && kc + E <= k) {
-          cw[u] = *reinterpret_cast<const uint4 *>(crow + off);
-        } else {
-          uint32_t t[4] = {0u, 0u, 0u, 0u};
+      for (int r = 0; r < RPW; ++r) {
+        const int64_t j = j0 + r < n ? j0 + r : n - 1;  // rows past n load a valid row; never stored
+        const uint8_t *crow = codes + j * row_bytes;
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (kc + (int64_t)(q + 1) * E / 4 <= k) t[q] = reinterpret_cast<const uint32_t *>(crow + off)[q];
-          cw[u] = make_uint4(t[0], t[1], t[2], t[3]);
+        for (int u = 0; u < U; ++u) {
+          const int64_t kc = kc0 + (int64_t)u * 64 * E;
+          const int64_t off = Traits<F>::kBits == 4 ? kc / 2 : kc;
+          if (VEC && kc + E <= k) {
+            cw[r][u] = *reinterpret_cast<const uint4 *>(crow + off);
+          } else {
+            uint32_t t[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (kc + (int64_t)(q + 1) * E / 4 <= k) t[q] = reinterpret_cast<const uint32_t *>(crow + off)[q];
+            cw[r][u] = make_uint4(t[0], t[1], t[2], t[3]);
+          }
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            const int64_t pb = kc + (int64_t)b * (E / NB);
+            const int64_t bi = pb < k ? pb / B : nblk - 1;
+            sr[r][u][b] = load_scale_raw<F>(scales, j * nblk + bi);
+          }
+          if constexpr (F == kINT4_AFFINE) br[r][u] = biases[j * nblk + (kc < k ? kc / B : nblk - 1)];
         }
       }
+      // ---- phase B: decode, dot, fold ----
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
+      for (int u = 0; u < U; ++u) {
         const int64_t kc = kc0 + (int64_t)u * 64 * E;
         if (kc >= k) break;
-        const uint32_t cwa[4] = {cw[u].x, cw[u].y, cw[u].z, cw[u].w};
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
           const int64_t pb = kc + (int64_t)b * (E / NB);
           if (pb >= k) break;
-          const float sc = load_scale<F>(scales, j * nblk + pb / B);
-          float bias = 0.0f;
-          if constexpr (F == kINT4_AFFINE) bias = bf16_bits_to_f32(biases[j * nblk + pb / B]);
-          float part[M], xsum[M];
+          float part[RPW][M], xsum[M];
 #pragma unroll
-          for (int mi = 0; mi < M; ++mi) part[mi] = xsum[mi] = 0.0f;
+          for (int mi = 0; mi < M; ++mi) {
+            xsum[mi] = 0.0f;
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) part[r][mi] = 0.0f;
+          }
 #pragma unroll
           for (int s = b * SPB; s < (b + 1) * SPB; ++s) {
             const int64_t p = kc + 8 * s;
             if (p >= k) break;
-            // code words of this sub-chunk: one word (4-bit) or two (8-bit)
-            const uint32_t w0 = Traits<F>::kBits == 4 ? cwa[s] : cwa[2 * s];
-            const uint32_t w1 = Traits<F>::kBits == 4 ? 0u : cwa[2 * s + 1];
 #pragma unroll
             for (int mi = 0; mi < M; ++mi) {
               if (i0 + mi >= m) break;
               if constexpr (XT == 1) {
                 const uint4 xq = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(xv) + (i0 + mi) * k + p);
-                part[mi] = dot8_bf16<F>(w0, w1, xq, part[mi]);
+#pragma unroll
+                for (int r = 0; r < RPW; ++r) {
+                  const uint32_t cwa[4] = {cw[r][u].x, cw[r][u].y, cw[r][u].z, cw[r][u].w};
+                  const uint32_t w0 = Traits<F>::kBits == 4 ? cwa[s] : cwa[2 * s];
+                  const uint32_t w1 = Traits<F>::kBits == 4 ? 0u : cwa[2 * s + 1];
+                  part[r][mi] = dot8_bf16<F>(w0, w1, xq, part[r][mi]);
+                }
                 if constexpr (F == kINT4_AFFINE) {
                   const uint32_t xs[4] = {xq.x, xq.y, xq.z, xq.w};
 #pragma unroll
@@ -196,7 +228,13 @@ rows_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
                 const float4 *xp = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(xv) + (i0 + mi) * k + p);
                 const float4 a = xp[0], c = xp[1];
                 const float xf[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-                part[mi] = dot8_f32<F>(w0, w1, xf, part[mi]);
+#pragma unroll
+                for (int r = 0; r < RPW; ++r) {
+                  const uint32_t cwa[4] = {cw[r][u].x, cw[r][u].y, cw[r][u].z, cw[r][u].w};
+                  const uint32_t w0 = Traits<F>::kBits == 4 ? cwa[s] : cwa[2 * s];
+                  const uint32_t w1 = Traits<F>::kBits == 4 ? 0u : cwa[2 * s + 1];
+                  part[r][mi] = dot8_f32<F>(w0, w1, xf, part[r][mi]);
+                }
                 if constexpr (F == kINT4_AFFINE) {
 #pragma unroll
                   for (int i = 0; i < 8; ++i) xsum[mi] += xf[i];
@@ -205,41 +243,60 @@ rows_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
             }
           }
 #pragma unroll
-          for (int mi = 0; mi < M; ++mi) {
-            acc[mi] = __builtin_fmaf(part[mi], sc, acc[mi]);
-            if constexpr (F == kINT4_AFFINE) acc[mi] = __builtin_fmaf(xsum[mi], bias, acc[mi]);
+          for (int r = 0; r < RPW; ++r) {
+            const float sc = scale_value<F>(sr[r][u][b]);
+#pragma unroll
+            for (int mi = 0; mi < M; ++mi) {
+              acc[r][mi] = __builtin_fmaf(part[r][mi], sc, acc[r][mi]);
+              if constexpr (F == kINT4_AFFINE) acc[r][mi] = __builtin_fmaf(xsum[mi], bf16_bits_to_f32(br[r][u]), acc[r][mi]);
+            }
           }
         }
       }
     }
 
 #pragma unroll
-    for (int mi = 0; mi < M; ++mi) {
-      float v = wave_sum(acc[mi]);
-      if constexpr (F == kNVFP4) v *= global;
-      if (lane == mi && i0 + mi < m) {
-        const int64_t o = (i0 + mi) * n + j;
-        if (ot == 0) reinterpret_cast<float *>(out)[o] = v;
-        else reinterpret_cast<uint16_t *>(out)[o] = f32_to_bf16_bits(v);
+    for (int r = 0; r < RPW; ++r) {
+#pragma unroll
+      for (int mi = 0; mi < M; ++mi) {
+        float v = wave_sum(acc[r][mi]);
+        if constexpr (F == kNVFP4) v *= global;
+        if (lane == r * M + mi && j0 + r < n && i0 + mi < m) {
+          const int64_t o = (i0 + mi) * n + j0 + r;
+          if (ot == 0) reinterpret_cast<float *>(out)[o] = v;
+          else reinterpret_cast<uint16_t *>(out)[o] = f32_to_bf16_bits(v);
+        }
       }
     }
   }
 }
 
-template <int F, int M, int XT>
-hipError_t run_m(const QWeight &w, int64_t m, const void *x, void *out, int ot, hipStream_t s) {
+template <int F, int M, int XT, int RPW, int U>
+hipError_t run_cfg(const QWeight &w, int64_t m, const void *x, void *out, int ot, hipStream_t s) {
   const bool vec = Traits<F>::kBits == 8 || (w.k % 32) == 0;  // 16-byte aligned code rows
-  int64_t wgs = (w.n + kWaves - 1) / kWaves;
+  const int64_t waves = (w.n + RPW - 1) / RPW;
+  int64_t wgs = (waves + kWaves - 1) / kWaves;
   if (wgs > 8192) wgs = 8192;
   const int64_t ychunks = (m + M - 1) / M;
   const dim3 grid((unsigned)wgs, (unsigned)ychunks);
   if (vec)
-    hipLaunchKernelGGL((rows_kernel<F, M, XT, true>), grid, dim3(kWaves * 64), 0, s, (const uint8_t *)w.codes,
+    hipLaunchKernelGGL((rows_kernel<F, M, XT, true, RPW, U>), grid, dim3(kWaves * 64), 0, s, (const uint8_t *)w.codes,
                        w.scales, (const uint16_t *)w.biases, w.global, x, out, ot, m, w.n, w.k);
   else
-    hipLaunchKernelGGL((rows_kernel<F, M, XT, false>), grid, dim3(kWaves * 64), 0, s, (const uint8_t *)w.codes,
+    hipLaunchKernelGGL((rows_kernel<F, M, XT, false, RPW, U>), grid, dim3(kWaves * 64), 0, s, (const uint8_t *)w.codes,
                        w.scales, (const uint16_t *)w.biases, w.global, x, out, ot, m, w.n, w.k);
   return hipGetLastError();
+}
+
+// Rows per wave and chunks per round: the bf16 decode GEMV (M <= 2) keeps
+// two rows' code loads in flight per wave (measured best for the 4096x4096
+// nvfp4 and 14336x4096 mxfp8 decode shapes); wider M reuses each decoded
+// chunk M times and keeps one row per wave to bound registers.
+template <int F, int M, int XT>
+hipError_t run_m(const QWeight &w, int64_t m, const void *x, void *out, int ot, hipStream_t s) {
+  constexpr int U = 2;  // 16-byte chunks per row per round
+  if constexpr (M <= 2 && XT == 1) return run_cfg<F, M, XT, 2, U>(w, m, x, out, ot, s);
+  else return run_cfg<F, M, XT, 1, U>(w, m, x, out, ot, s);
 }
 
 template <int F, int XT>
