@@ -101,7 +101,7 @@ def time_workload(wl, steps, warmup, device, rotate=True, per_graph=None):
 
     d = setup(wl, device, rotate)
     if per_graph is None:
-        per_graph = d["copies"] if wl.op == "qgemv" else 1
+        per_graph = d["copies"] if wl.op == "qgemv" else (4 if wl.m > 8 else 64)
     per_graph = max(1, min(per_graph, steps))
     stream = torch.cuda.Stream(device)
     torch.cuda.synchronize(device)
@@ -183,6 +183,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only-timed", action="store_true", help="timed workload only (for profiling)")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
+                    help="only run torch's copy kernel on MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (this build has no multi-GPU "
@@ -194,6 +196,17 @@ def main():
     from block_scaled_bit_e2m1_amd import bsq, workloads
 
     device = torch.device("cuda:0")
+    if args.calib_copy:
+        # A plain device copy of known size: its FETCH_SIZE / WRITE_SIZE
+        # counters calibrate the byte counters of the timed kernels.
+        n = args.calib_copy << 20
+        src = torch.ones(n // 4, dtype=torch.int32, device=device)
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize(device)
+        print(json.dumps({"calib_copy_bytes": n, "launches": max(1, args.steps)}), flush=True)
+        return
     bsq.lib()
     wl = workloads.WORKLOADS[args.workload]
     kind = "qgemv" if wl.op == "qgemv" else "qgemm"

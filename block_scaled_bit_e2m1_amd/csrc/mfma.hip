@@ -444,12 +444,13 @@ hipError_t run_cfg(const QWeight &w, int64_t m, const void *x, void *out, int ot
 
 template <int F>
 hipError_t run_f(const QWeight &w, int64_t m, const void *x, void *out, int ot, hipStream_t s) {
-  if ((m + 127) / 128 * ((w.n + 127) / 128) > (int64_t)1 << 30) return hipErrorInvalidValue;
-  // 256x128 tiles when they fill the 256 CUs, 128x128 otherwise.  Both use
-  // 2x2 waves, a two-deep register prefetch and the phased step schedule.
+  if ((m + 127) / 128 * ((w.n + 63) / 64) > (int64_t)1 << 30) return hipErrorInvalidValue;
+  // 256x128 tiles when they fill the 256 CUs (best measured at m=2048,
+  // n=k=4096); otherwise 128x64 tiles, which run ~3 workgroups per CU and
+  // balance ragged tile counts (best measured at m=512, n=11008, k=4096).
   const int64_t big = ((m + 255) / 256) * ((w.n + 127) / 128);
   if (big >= 256) return run_cfg<F, 256, 128, 2, 2, 2, 4, false, 4>(w, m, x, out, ot, s);
-  return run_cfg<F, 128, 128, 2, 2, 2, 4, false, 4>(w, m, x, out, ot, s);
+  return run_cfg<F, 128, 64, 2, 2, 2, 4, false, 4>(w, m, x, out, ot, s);
 }
 
 }  // namespace
