@@ -9,10 +9,10 @@
 //
 // Geometry (gfx950, wave64): a wave owns RPW weight rows at a time.  Lane l
 // takes 16-byte code chunks l, l+64, l+128, ... along k (32 elements for 4-bit
-// codes, 16 for 8-bit).  The code and scale loads of U chunks of all RPW rows
-// are issued before any is used, so a wave keeps RPW*U HBM requests in flight
-// and the whole weight of a decode GEMV is requested in one round.  Per
-// 8-element sub-chunk the
+// codes, 16 for 8-bit).  The code, scale and X loads of a round (U chunks of
+// all RPW rows) are issued back to back before any arithmetic; full rounds
+// carry no bounds checks, so no wait separates them.  Per 8-element sub-chunk
+// the
 // unscaled element values are dotted with X in fp32; the block scale is folded
 // once per block ("fold in that block's scale ONCE (not per element)" [rlx-cpu
 // quant.rs, dequant_matmul_int8]) and the nvfp4 global once at the end
@@ -26,6 +26,8 @@
 // X and the integer formats use the branch-free software decoders and fp32 FMA.
 #include "bsq_internal.hpp"
 #include "codec.hpp"
+
+#include <type_traits>
 
 namespace bsq {
 namespace {
@@ -128,11 +130,12 @@ __device__ __forceinline__ float scale_value(uint32_t raw) {
   else return bf16_bits_to_f32(raw);
 }
 
-// A wave owns RPW consecutive weight rows.  Per round it issues the 16-byte
-// code loads (U chunks per row) and the scale loads of all RPW rows before
-// any arithmetic, so every HBM request of the round is in flight at once;
-// X (resident in L2) is loaded per 8-element sub-chunk and shared by the RPW
-// rows.
+// A wave owns RPW consecutive weight rows.  A round covers U 16-byte code
+// chunks per lane of each row.  Full rounds (every chunk inside k) are
+// branch-free: all code, scale (and, when it fits in registers, X) loads of
+// the round are issued before any arithmetic, so each wave keeps RPW*U HBM
+// requests in flight with no wait between them.  A ragged last round runs
+// the same code with bounds guards.
 template <int F, int M, int XT, bool VEC, int RPW, int U>
 __global__ void __launch_bounds__(kWaves * 64)
 rows_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, const uint16_t *__restrict__ biases,
@@ -142,12 +145,19 @@ rows_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
   constexpr int NSUB = E / 8;                           // 8-element sub-chunks per chunk
   constexpr int NB = B < E ? E / B : 1;                 // scale blocks per chunk
   constexpr int SPB = NSUB / NB;                        // sub-chunks per scale block
+  constexpr int XW = XT == 1 ? 1 : 2;                   // uint4 per 8 X values
+  constexpr bool XPRE = M * U * NSUB * XW <= 16;        // X of a round fits in 64 VGPRs
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * kWaves;
   const int64_t i0 = (int64_t)blockIdx.y * M;  // first X row of this launch chunk
   const int64_t nblk = k / B;
   const int64_t row_bytes = Traits<F>::kBits == 4 ? k / 2 : k;
+  const int64_t per_round = (int64_t)64 * E * U;
+  const int64_t full_rounds = VEC ? k / per_round : 0;
+  int64_t xrow[M];
+#pragma unroll
+  for (int mi = 0; mi < M; ++mi) xrow[mi] = (i0 + mi < m ? i0 + mi : m - 1) * k;  // rows past m: valid, unused
 
   for (int64_t j0 = wave * RPW; j0 < n; j0 += nwaves * RPW) {
     float acc[RPW][M];
@@ -155,20 +165,24 @@ rows_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
     for (int r = 0; r < RPW; ++r)
 #pragma unroll
       for (int mi = 0; mi < M; ++mi) acc[r][mi] = 0.0f;
+    int64_t jr[RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) jr[r] = j0 + r < n ? j0 + r : n - 1;  // rows past n: valid, never stored
 
-    for (int64_t kc0 = (int64_t)lane * E; kc0 < k; kc0 += (int64_t)64 * E * U) {
-      // ---- phase A: every HBM load of the round ----
+    auto round = [&](auto guard, int64_t kc0) {
+      constexpr bool kG = decltype(guard)::value;
+      // ---- phase A: the round's loads ----
       uint4 cw[RPW][U];
       uint32_t sr[RPW][U][NB], br[RPW][U];
+      uint4 xq[XPRE ? M : 1][XPRE ? U : 1][XPRE ? NSUB * XW : 1];
 #pragma unroll
       for (int r = 0; r < RPW; ++r) {
-        const int64_t j = j0 + r < n ? j0 + r : n - 1;  // rows past n load a valid row; never stored
-        const uint8_t *crow = codes + j * row_bytes;
+        const uint8_t *crow = codes + jr[r] * row_bytes;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int64_t kc = kc0 + (int64_t)u * 64 * E;
           const int64_t off = Traits<F>::kBits == 4 ? kc / 2 : kc;
-          if (VEC && kc + E <= k) {
+          if (!kG) {
             cw[r][u] = *reinterpret_cast<const uint4 *>(crow + off);
           } else {
             uint32_t t[4] = {0u, 0u, 0u, 0u};
@@ -180,21 +194,41 @@ rows_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
 #pragma unroll
           for (int b = 0; b < NB; ++b) {
             const int64_t pb = kc + (int64_t)b * (E / NB);
-            const int64_t bi = pb < k ? pb / B : nblk - 1;
-            sr[r][u][b] = load_scale_raw<F>(scales, j * nblk + bi);
+            const int64_t bi = (!kG || pb < k) ? pb / B : nblk - 1;
+            sr[r][u][b] = load_scale_raw<F>(scales, jr[r] * nblk + bi);
           }
-          if constexpr (F == kINT4_AFFINE) br[r][u] = biases[j * nblk + (kc < k ? kc / B : nblk - 1)];
+          if constexpr (F == kINT4_AFFINE) br[r][u] = biases[jr[r] * nblk + ((!kG || kc < k) ? kc / B : nblk - 1)];
         }
       }
+      if constexpr (XPRE) {
+#pragma unroll
+        for (int mi = 0; mi < M; ++mi)
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int q = 0; q < NSUB * XW; ++q) {
+              const int64_t p = kc0 + (int64_t)u * 64 * E + (q / XW) * 8;
+              if (!kG || p < k) {
+                if constexpr (XT == 1)
+                  xq[mi][u][q] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(xv) + xrow[mi] + p);
+                else
+                  xq[mi][u][q] = reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(xv) + xrow[mi] + p)[q % XW];
+              } else {
+                xq[mi][u][q] = make_uint4(0, 0, 0, 0);
+              }
+            }
+      }
+      // keep every load of the round ahead of the arithmetic
+      __builtin_amdgcn_sched_barrier(0);
       // ---- phase B: decode, dot, fold ----
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int64_t kc = kc0 + (int64_t)u * 64 * E;
-        if (kc >= k) break;
+        if (kG && kc >= k) break;
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
           const int64_t pb = kc + (int64_t)b * (E / NB);
-          if (pb >= k) break;
+          if (kG && pb >= k) break;
           float part[RPW][M], xsum[M];
 #pragma unroll
           for (int mi = 0; mi < M; ++mi) {
@@ -205,39 +239,45 @@ rows_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
 #pragma unroll
           for (int s = b * SPB; s < (b + 1) * SPB; ++s) {
             const int64_t p = kc + 8 * s;
-            if (p >= k) break;
+            if (kG && p >= k) break;
 #pragma unroll
             for (int mi = 0; mi < M; ++mi) {
               if (i0 + mi >= m) break;
-              if constexpr (XT == 1) {
-                const uint4 xq = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(xv) + (i0 + mi) * k + p);
+              uint4 xa, xb2;
+              if constexpr (XPRE) {
+                xa = xq[mi][u][s * XW];
+                xb2 = xq[mi][u][s * XW + XW - 1];
+              } else if constexpr (XT == 1) {
+                xa = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(xv) + xrow[mi] + p);
+                xb2 = xa;
+              } else {
+                const uint4 *xp = reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(xv) + xrow[mi] + p);
+                xa = xp[0];
+                xb2 = xp[1];
+              }
 #pragma unroll
-                for (int r = 0; r < RPW; ++r) {
-                  const uint32_t cwa[4] = {cw[r][u].x, cw[r][u].y, cw[r][u].z, cw[r][u].w};
-                  const uint32_t w0 = Traits<F>::kBits == 4 ? cwa[s] : cwa[2 * s];
-                  const uint32_t w1 = Traits<F>::kBits == 4 ? 0u : cwa[2 * s + 1];
-                  part[r][mi] = dot8_bf16<F>(w0, w1, xq, part[r][mi]);
+              for (int r = 0; r < RPW; ++r) {
+                const uint32_t cwa[4] = {cw[r][u].x, cw[r][u].y, cw[r][u].z, cw[r][u].w};
+                const uint32_t w0 = Traits<F>::kBits == 4 ? cwa[s] : cwa[2 * s];
+                const uint32_t w1 = Traits<F>::kBits == 4 ? 0u : cwa[2 * s + 1];
+                if constexpr (XT == 1) {
+                  part[r][mi] = dot8_bf16<F>(w0, w1, xa, part[r][mi]);
+                } else {
+                  const float xf[8] = {__uint_as_float(xa.x), __uint_as_float(xa.y), __uint_as_float(xa.z),
+                                       __uint_as_float(xa.w), __uint_as_float(xb2.x), __uint_as_float(xb2.y),
+                                       __uint_as_float(xb2.z), __uint_as_float(xb2.w)};
+                  part[r][mi] = dot8_f32<F>(w0, w1, xf, part[r][mi]);
                 }
-                if constexpr (F == kINT4_AFFINE) {
-                  const uint32_t xs[4] = {xq.x, xq.y, xq.z, xq.w};
+              }
+              if constexpr (F == kINT4_AFFINE) {
+                if constexpr (XT == 1) {
+                  const uint32_t xs[4] = {xa.x, xa.y, xa.z, xa.w};
 #pragma unroll
                   for (int i = 0; i < 4; ++i)
                     xsum[mi] += __uint_as_float(xs[i] << 16) + __uint_as_float(xs[i] & 0xFFFF0000u);
-                }
-              } else {
-                const float4 *xp = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(xv) + (i0 + mi) * k + p);
-                const float4 a = xp[0], c = xp[1];
-                const float xf[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-#pragma unroll
-                for (int r = 0; r < RPW; ++r) {
-                  const uint32_t cwa[4] = {cw[r][u].x, cw[r][u].y, cw[r][u].z, cw[r][u].w};
-                  const uint32_t w0 = Traits<F>::kBits == 4 ? cwa[s] : cwa[2 * s];
-                  const uint32_t w1 = Traits<F>::kBits == 4 ? 0u : cwa[2 * s + 1];
-                  part[r][mi] = dot8_f32<F>(w0, w1, xf, part[r][mi]);
-                }
-                if constexpr (F == kINT4_AFFINE) {
-#pragma unroll
-                  for (int i = 0; i < 8; ++i) xsum[mi] += xf[i];
+                } else {
+                  xsum[mi] += ((__uint_as_float(xa.x) + __uint_as_float(xa.y)) + (__uint_as_float(xa.z) + __uint_as_float(xa.w))) +
+                              ((__uint_as_float(xb2.x) + __uint_as_float(xb2.y)) + (__uint_as_float(xb2.z) + __uint_as_float(xb2.w)));
                 }
               }
             }
@@ -253,7 +293,11 @@ rows_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
           }
         }
       }
-    }
+    };
+
+    const int64_t lane0 = (int64_t)lane * E;
+    for (int64_t rr = 0; rr < full_rounds; ++rr) round(std::integral_constant<bool, false>{}, lane0 + rr * per_round);
+    if (full_rounds * per_round < k) round(std::integral_constant<bool, true>{}, lane0 + full_rounds * per_round);
 
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
@@ -289,14 +333,15 @@ hipError_t run_cfg(const QWeight &w, int64_t m, const void *x, void *out, int ot
 }
 
 // Rows per wave and chunks per round: the bf16 decode GEMV (M <= 2) keeps
-// two rows' code loads in flight per wave (measured best for the 4096x4096
-// nvfp4 and 14336x4096 mxfp8 decode shapes); wider M reuses each decoded
-// chunk M times and keeps one row per wave to bound registers.
+// two rows' code loads in flight per wave, one chunk per row and round for
+// 4-bit codes and two for 8-bit codes (measured best on the 4096x4096 nvfp4
+// and 14336x4096 mxfp8 decode shapes); wider M reuses each decoded chunk M
+// times and keeps one row per wave to bound registers.
 template <int F, int M, int XT>
 hipError_t run_m(const QWeight &w, int64_t m, const void *x, void *out, int ot, hipStream_t s) {
-  constexpr int U = 2;  // 16-byte chunks per row per round
+  constexpr int U = Traits<F>::kBits == 4 ? 1 : 2;  // 16-byte chunks per row per round
   if constexpr (M <= 2 && XT == 1) return run_cfg<F, M, XT, 2, U>(w, m, x, out, ot, s);
-  else return run_cfg<F, M, XT, 1, U>(w, m, x, out, ot, s);
+  else return run_cfg<F, M, XT, 1, 2>(w, m, x, out, ot, s);
 }
 
 template <int F, int XT>
