@@ -31,7 +31,7 @@ PATH_AUTO, PATH_ROWS, PATH_MFMA = 0, 1, 2
 # bsq_status
 OK, ERR_ARG, ERR_UNSUPPORTED, ERR_SHAPE, ERR_ALIGN, ERR_NONFINITE, ERR_HIP = 0, 1, 2, 3, 4, 5, 6
 
-EXPORTS = ["bsq_packed_bytes", "bsq_pack_host", "bsq_dequant", "bsq_qgemv", "bsq_qgemm", "bsq_qgemm_path",
+EXPORTS = ["bsq_packed_bytes", "bsq_pack_host", "bsq_quantize", "bsq_dequant", "bsq_qgemv", "bsq_qgemm", "bsq_qgemm_path",
            "bsq_status_string", "bsq_last_error", "bsq_version"]
 
 
@@ -54,11 +54,12 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         L.bsq_packed_bytes.argtypes = [_c_int, _c_int, _i64, _i64, _sz, _sz, _sz]
         L.bsq_pack_host.argtypes = [_c_int, _c_int, _vp, _i64, _i64, _vp, _vp, _vp, ctypes.POINTER(_f32)]
+        L.bsq_quantize.argtypes = [_c_int, _c_int, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]
         L.bsq_dequant.argtypes = [_c_int, _c_int, _i64, _i64, _vp, _vp, _vp, _f32, _vp, _vp]
         L.bsq_qgemv.argtypes = [_c_int, _c_int, _i64, _i64, _vp, _vp, _vp, _f32, _vp, _c_int, _vp, _c_int, _vp]
         L.bsq_qgemm.argtypes = [_c_int, _c_int, _i64, _i64, _i64, _vp, _vp, _vp, _f32, _vp, _c_int, _vp, _c_int, _vp]
         L.bsq_qgemm_path.argtypes = [_c_int] + L.bsq_qgemm.argtypes
-        for f in ("bsq_packed_bytes", "bsq_pack_host", "bsq_dequant", "bsq_qgemv", "bsq_qgemm", "bsq_qgemm_path"):
+        for f in ("bsq_packed_bytes", "bsq_pack_host", "bsq_quantize", "bsq_dequant", "bsq_qgemv", "bsq_qgemm", "bsq_qgemm_path"):
             getattr(L, f).restype = _c_int
         for f in ("bsq_status_string", "bsq_last_error", "bsq_version"):
             getattr(L, f).restype = ctypes.c_char_p
@@ -78,6 +79,10 @@ def bsq_packed_bytes(fmt, block, n, k):
 
 def bsq_pack_host(fmt, block, w, n, k, codes, scales, biases, global_out):
     return lib().bsq_pack_host(fmt, block, w, n, k, codes, scales, biases, global_out)
+
+
+def bsq_quantize(fmt, block, w, n, k, codes, scales, biases, global_dev, status_dev, stream):
+    return lib().bsq_quantize(fmt, block, w, n, k, codes, scales, biases, global_dev, status_dev, stream)
 
 
 def bsq_dequant(fmt, block, n, k, codes, scales, biases, global_scale, out, stream):
@@ -170,6 +175,28 @@ def pack(fmt, w, block: int = 0) -> PackedWeight:
                        ctypes.byref(g))
     _check(st, "bsq_pack_host")
     return PackedWeight(f, n, k, codes, scales, biases, float(g.value))
+
+
+def quantize(fmt, w: torch.Tensor, block: int = 0, check_finite: bool = True) -> PackedWeight:
+    """Pack a device f32 [n,k] weight on the GPU (bsq_quantize).  The nvfp4
+    global scale is read back to the host (one synchronizing copy)."""
+    f = _fmt(fmt)
+    if w.dtype != torch.float32 or not w.is_cuda or not w.is_contiguous():
+        raise ValueError("w must be a contiguous float32 CUDA tensor")
+    n, k = w.shape
+    cb, sb, bb = packed_bytes(f, n, k, block)
+    dev = w.device
+    codes = torch.empty(max(cb, 16), dtype=torch.uint8, device=dev)[:cb]
+    scales = torch.empty(max(sb, 4), dtype=torch.uint8, device=dev)[:sb]
+    biases = torch.empty(max(bb, 2), dtype=torch.uint8, device=dev)[:bb] if bb else None
+    gdev = torch.ones(1, dtype=torch.float32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    st = bsq_quantize(f, block, _ptr(w), n, k, _ptr(codes), _ptr(scales), _ptr(biases), _ptr(gdev),
+                      _ptr(status) if check_finite else None, _stream(dev))
+    _check(st, "bsq_quantize")
+    if check_finite and int(status.item()) != OK:
+        raise BsqError(int(status.item()), "bsq_quantize (device)")
+    return PackedWeight(f, n, k, codes, scales, biases, float(gdev.item()) if f == NVFP4 else 1.0)
 
 
 def to_device(pw: PackedWeight, device="cuda") -> PackedWeight:

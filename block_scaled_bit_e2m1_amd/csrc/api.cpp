@@ -127,6 +127,24 @@ bsq_status bsq_pack_host(bsq_format fmt, int block, const float *w, int64_t n, i
   return ok();
 }
 
+bsq_status bsq_quantize(bsq_format fmt, int block, const float *w, int64_t n, int64_t k, void *codes, void *scales,
+                        void *biases, float *global_dev, int *status_dev, void *stream) {
+  bsq_status s;
+  if ((s = check_format(fmt, block))) return s;
+  if ((s = check_shape(fmt, n, k))) return s;
+  if (n == 0 || k == 0) return ok();
+  if (!w || !codes || !scales) return fail(BSQ_ERR_ARG, "null pointer");
+  if (fmt == BSQ_INT4_AFFINE && !biases) return fail(BSQ_ERR_ARG, "int4 affine needs biases");
+  if (fmt == BSQ_NVFP4 && !global_dev) return fail(BSQ_ERR_ARG, "nvfp4 needs a device float for the global scale");
+  if (!aligned(w, 16) || !aligned(codes, 16)) return fail(BSQ_ERR_ALIGN, "w and codes must be 16-byte aligned");
+  if (!aligned(scales, scale_elem_bytes(fmt)) || (biases && !aligned(biases, 2)) ||
+      (global_dev && !aligned(global_dev, 4)) || (status_dev && !aligned(status_dev, 4)))
+    return fail(BSQ_ERR_ALIGN, "scales, biases, global or status misaligned");
+  return hip_status(bsq::launch_quantize(fmt, w, n, k, codes, scales, biases, global_dev, status_dev,
+                                         (hipStream_t)stream),
+                    "quantize launch");
+}
+
 bsq_status bsq_dequant(bsq_format fmt, int block, int64_t n, int64_t k, const void *codes, const void *scales,
                        const void *biases, float global_scale, float *out, void *stream) {
   bsq_status s;

@@ -53,6 +53,12 @@ hipError_t launch_mfma(const QWeight &w, int64_t m, const void *x, void *out, in
 // Zero-fill an output of `bytes` bytes (k == 0 case).
 hipError_t launch_zero(void *out, int64_t bytes, hipStream_t s);
 
+// Device packer (quantize.hip): the host packer's encoding on the GPU.  gdev
+// (nvfp4) receives the global scale; status (may be null) receives 5 if a
+// block holds a non-finite value.
+hipError_t launch_quantize(int fmt, const float *w, int64_t n, int64_t k, void *codes, void *scales, void *biases,
+                           float *gdev, int *status, hipStream_t s);
+
 // Host packer (pack_host.cpp).  Returns a bsq_status value.
 int pack_host(int fmt, const float *w, int64_t n, int64_t k, void *codes, void *scales, void *biases,
               float *global_out);

@@ -1,0 +1,142 @@
+// quantize.hip -- device packer: f32 W [n,k] in HBM -> codes + block scales.
+//
+// The same encoding as the host packer (pack_math.hpp: per-block scale from
+// the block amax, codes against the stored scale, fp64 quotients), computed on
+// the GPU so a weight never has to visit the host to be re-packed
+// [rlx-cpu quant.rs, lowp_compute_scales and lowp_quantize, which the pages
+// run as producer ops of the scaled matmul].
+//
+// One thread packs one block: it reads the block's B floats (16-byte loads,
+// adjacent threads on adjacent blocks), encodes, and writes the block's codes
+// (B/2 or B bytes) and its scale.  nvfp4 first reduces the tensor amax into
+// the caller's device float (vector atomicMax on the bits of non-negative
+// floats), then turns it into the global scale in place.
+#include "bsq_internal.hpp"
+#include "pack_math.hpp"
+
+namespace bsq {
+namespace {
+
+__global__ void amax_init(float *g) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) *g = 0.0f;
+}
+
+__global__ void __launch_bounds__(256) amax_kernel(const float4 *__restrict__ w, int64_t n4, unsigned *__restrict__ g) {
+  float a = 0.0f;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+    const float4 v = w[i];
+    a = fmaxf(a, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+  }
+  // wave-level max first: one atomic per wave
+  for (int o = 32; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
+  if ((threadIdx.x & 63) == 0) atomicMax(g, __float_as_uint(a));
+}
+
+__global__ void global_finalize(float *g) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) *g = pk::nvfp4_global(*g);
+}
+
+template <int F>
+__global__ void __launch_bounds__(256)
+quantize_kernel(const float *__restrict__ w, int64_t n, int64_t k, const float *__restrict__ gdev,
+                uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, uint8_t *__restrict__ biases,
+                int *__restrict__ status) {
+  constexpr int B = Traits<F>::kBlock;
+  const int64_t nb = k / B, blocks = n * nb;
+  const float g = (F == kNVFP4) ? *gdev : 1.0f;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < blocks; t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t j = t / nb, b = t - j * nb;
+    const float *src = w + j * k + b * B;
+    float x[B];
+#pragma unroll
+    for (int i = 0; i < B; i += 4) {
+      const float4 v = *reinterpret_cast<const float4 *>(src + i);
+      x[i] = v.x;
+      x[i + 1] = v.y;
+      x[i + 2] = v.z;
+      x[i + 3] = v.w;
+    }
+    bool finite = true;
+#pragma unroll
+    for (int i = 0; i < B; ++i) finite = finite && isfinite(x[i]);
+    if (!finite && status) *status = 5;  // BSQ_ERR_NONFINITE; the block's bytes are then unspecified
+    uint8_t c[B];
+    uint32_t sb, bb;
+    pk::pack_block<F>(x, g, c, &sb, &bb);
+    const int64_t p0 = j * k + b * B;
+    if constexpr (Traits<F>::kBits == 4) {
+      uint32_t words[B / 8];
+#pragma unroll
+      for (int q = 0; q < B / 8; ++q) {
+        uint32_t wd = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) wd |= (uint32_t)(c[8 * q + i] & 0xF) << (4 * i);
+        words[q] = wd;
+      }
+      uint32_t *dst = reinterpret_cast<uint32_t *>(codes + p0 / 2);
+      if constexpr (B / 8 == 2) {
+        *reinterpret_cast<uint2 *>(dst) = make_uint2(words[0], words[1]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < B / 8; q += 4)
+          *reinterpret_cast<uint4 *>(dst + q) = make_uint4(words[q], words[q + 1], words[q + 2], words[q + 3]);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < B; q += 16) {
+        uint32_t wd[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          wd[r] = (uint32_t)c[q + 4 * r] | ((uint32_t)c[q + 4 * r + 1] << 8) | ((uint32_t)c[q + 4 * r + 2] << 16) |
+                  ((uint32_t)c[q + 4 * r + 3] << 24);
+        *reinterpret_cast<uint4 *>(codes + p0 + q) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+      }
+    }
+    if constexpr (F == kNVFP8 || F == kINT8_SYM) {
+      reinterpret_cast<uint32_t *>(scales)[t] = sb;
+    } else if constexpr (F == kINT4_AFFINE) {
+      reinterpret_cast<uint16_t *>(scales)[t] = (uint16_t)sb;
+      reinterpret_cast<uint16_t *>(biases)[t] = (uint16_t)bb;
+    } else {
+      scales[t] = (uint8_t)sb;
+    }
+  }
+}
+
+template <int F>
+hipError_t run(const float *w, int64_t n, int64_t k, void *codes, void *scales, void *biases, float *gdev,
+               int *status, hipStream_t s) {
+  if constexpr (F == kNVFP4) {
+    hipLaunchKernelGGL(amax_init, dim3(1), dim3(64), 0, s, gdev);
+    const int64_t n4 = n * k / 4;
+    int64_t blocks = (n4 + 255) / 256;
+    if (blocks > 2048) blocks = 2048;
+    hipLaunchKernelGGL(amax_kernel, dim3((unsigned)blocks), dim3(256), 0, s, reinterpret_cast<const float4 *>(w), n4,
+                       reinterpret_cast<unsigned *>(gdev));
+    hipLaunchKernelGGL(global_finalize, dim3(1), dim3(64), 0, s, gdev);
+  }
+  const int64_t nblocks = n * (k / Traits<F>::kBlock);
+  int64_t grid = (nblocks + 255) / 256;
+  if (grid > 65536) grid = 65536;
+  hipLaunchKernelGGL(quantize_kernel<F>, dim3((unsigned)grid), dim3(256), 0, s, w, n, k, gdev, (uint8_t *)codes,
+                     (uint8_t *)scales, (uint8_t *)biases, status);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize(int fmt, const float *w, int64_t n, int64_t k, void *codes, void *scales, void *biases,
+                           float *gdev, int *status, hipStream_t s) {
+  switch (fmt) {
+    case kMXFP4: return run<kMXFP4>(w, n, k, codes, scales, biases, gdev, status, s);
+    case kNVFP4: return run<kNVFP4>(w, n, k, codes, scales, biases, gdev, status, s);
+    case kMXFP8_E4M3: return run<kMXFP8_E4M3>(w, n, k, codes, scales, biases, gdev, status, s);
+    case kMXFP8_E5M2: return run<kMXFP8_E5M2>(w, n, k, codes, scales, biases, gdev, status, s);
+    case kNVFP8: return run<kNVFP8>(w, n, k, codes, scales, biases, gdev, status, s);
+    case kINT4_AFFINE: return run<kINT4_AFFINE>(w, n, k, codes, scales, biases, gdev, status, s);
+    case kINT8_SYM: return run<kINT8_SYM>(w, n, k, codes, scales, biases, gdev, status, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace bsq

@@ -101,6 +101,20 @@ bsq_status bsq_packed_bytes(bsq_format fmt, int block, int64_t n, int64_t k, siz
 bsq_status bsq_pack_host(bsq_format fmt, int block, const float *w, int64_t n, int64_t k, void *codes,
                          void *scales, void *biases, float *global_out);
 
+/* Device packer: the same encoding as bsq_pack_host (byte-identical output),
+ * computed on the GPU from a weight already in HBM -- the quantize producer
+ * of the pages' scaled-matmul ops [rlx-cpu quant.rs, lowp_compute_scales /
+ * lowp_quantize; metaltile PR #250, QFormat pack commit].
+ * w: device f32 [n,k], 16-byte aligned.  codes/scales/biases: device buffers
+ * sized by bsq_packed_bytes (biases for int4 only).  global_dev: device float,
+ * required for nvfp4 (receives f32(T/2688) computed from the tensor amax T on
+ * the device; the caller reads it back if it needs it on the host), ignored
+ * otherwise.  status_dev: optional device int that the kernel sets to
+ * BSQ_ERR_NONFINITE if any weight is NaN or inf (that block's bytes are then
+ * unspecified); the caller initialises it.  Asynchronous on `stream`. */
+bsq_status bsq_quantize(bsq_format fmt, int block, const float *w, int64_t n, int64_t k, void *codes, void *scales,
+                        void *biases, float *global_dev, int *status_dev, void *stream);
+
 /* Standalone dequant: out (device f32 [n,k]) = decode(code) * scale with one
  * rounding to f32 (nvfp4: (e2m1 * e4m3) * global; int4: s*q + b)
  * [metaltile PR #250, "First spec-conformant block-scaled dequant kernel" and

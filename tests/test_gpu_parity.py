@@ -322,3 +322,41 @@ def test_graph_replay_matches_eager():
             torch.cuda.synchronize()
         outs[fmt] = True
     assert len(outs) == 3
+
+
+# ----------------------------------------------------------------- device quantize
+@pytest.mark.parametrize("fmt", ALL)
+def test_device_quantize_equals_oracle_pack(fmt):
+    """bsq_quantize on the GPU writes the oracle's pack bytes exactly."""
+    rng = np.random.default_rng(91)
+    cases = [workloads.random_weights(96, 1024, seed=17, sigma=0.02, outliers=True),
+             (rng.standard_normal((40, 256)) * np.exp(rng.uniform(-30, 30, (40, 1)))).astype(np.float32)]
+    w = cases[1]
+    w[0] = 0
+    w[1, :64] = -0.0
+    w[2] = np.float32(3.4e38) * np.sign(rng.standard_normal(256)).astype(np.float32)
+    w[3] = np.float32(1e-45)
+    w[4, ::2] = 6.0
+    w[5] = np.linspace(-7, 7, 256, dtype=np.float32)
+    for W in cases:
+        p = oracle.pack(fmt, W)
+        q = bsq.quantize(fmt, torch.from_numpy(W).to(DEV))
+        assert (q.codes.cpu().numpy() == p["codes"]).all()
+        assert (q.scales.cpu().numpy() == p["scales"]).all()
+        if p["biases"] is not None:
+            assert (q.biases.cpu().numpy() == p["biases"]).all()
+        assert q.global_scale == p["global"]
+
+
+def test_device_quantize_workload_sizes_and_nonfinite():
+    for name in ["nvfp4_qgemv_4096", "mxfp4_qgemm_2048", "int4_affine_qgemm_512"]:
+        wl = workloads.WORKLOADS[name]
+        W, _ = workloads.generate(wl, m=1)
+        p = oracle.pack(wl.fmt, W)
+        q = bsq.quantize(wl.fmt, torch.from_numpy(W).to(DEV))
+        assert (q.codes.cpu().numpy() == p["codes"]).all() and (q.scales.cpu().numpy() == p["scales"]).all(), name
+    W = np.ones((4, 64), np.float32)
+    W[2, 5] = np.nan
+    with pytest.raises(bsq.BsqError) as e:
+        bsq.quantize("mxfp4", torch.from_numpy(W).to(DEV))
+    assert e.value.status == bsq.ERR_NONFINITE
