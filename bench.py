@@ -141,6 +141,42 @@ def hot_time(wl, device, iters=200):
     return r["event_ms"]
 
 
+def time_quantize(device, fmt="mxfp4", n=4096, k=4096, launches=200):
+    """Device-side pack of an f32 weight already in HBM (bsq_quantize):
+    bytes = f32 read + codes/scales written, per launch."""
+    import torch
+
+    from block_scaled_bit_e2m1_amd import bsq, workloads
+
+    W = torch.from_numpy(workloads.random_weights(n, k, seed=1003, sigma=0.02)).to(device)
+    q = bsq.quantize(fmt, W)
+    status = torch.zeros(1, dtype=torch.int32, device=device)
+    gdev = torch.ones(1, dtype=torch.float32, device=device)
+    stream = torch.cuda.Stream(device)
+
+    def one():
+        st = bsq.bsq_quantize(q.fmt, 0, bsq._ptr(W), bsq.F32, n, k, bsq._ptr(q.codes), bsq._ptr(q.scales),
+                              bsq._ptr(q.biases), bsq._ptr(gdev), bsq._ptr(status), bsq._stream(device))
+        assert st == bsq.OK
+
+    with torch.cuda.stream(stream):
+        for _ in range(5):
+            one()
+    torch.cuda.synchronize(device)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(launches):
+            one()
+        e1.record(stream)
+    torch.cuda.synchronize(device)
+    us = e0.elapsed_time(e1) * 1e3 / launches
+    nbytes = n * k * 4 + q.weight_bytes
+    return {"workload": f"quantize_{fmt}_{n}x{k}", "note": "device pack of an f32 weight (bsq_quantize)",
+            "value": round(nbytes / (us * 1e-6) / 1e9, 2), "unit": "GB/s", "us_per_launch": round(us, 3),
+            "roofline_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def cpu_baseline(wl, budget_s=10.0):
     """The oracle as it stands (dequant, then fp64 dot) on the host cores."""
     import numpy as np
@@ -257,6 +293,9 @@ def main():
             log(f"  {name}: {v:.2f} {u} ({r2['event_ms'] * 1e3:.2f} us/launch)")
             del r2
             torch.cuda.empty_cache()
+
+    if not args.no_extra and not args.only_timed:
+        extra.append(time_quantize(device))
 
     cpu = None
     if not args.no_cpu and not args.only_timed:

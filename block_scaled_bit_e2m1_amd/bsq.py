@@ -32,7 +32,7 @@ PATH_AUTO, PATH_ROWS, PATH_MFMA = 0, 1, 2
 OK, ERR_ARG, ERR_UNSUPPORTED, ERR_SHAPE, ERR_ALIGN, ERR_NONFINITE, ERR_HIP = 0, 1, 2, 3, 4, 5, 6
 
 EXPORTS = ["bsq_packed_bytes", "bsq_pack_host", "bsq_quantize", "bsq_dequant", "bsq_qgemv", "bsq_qgemm", "bsq_qgemm_path",
-           "bsq_status_string", "bsq_last_error", "bsq_version"]
+           "bsq_qgemm_mx", "bsq_status_string", "bsq_last_error", "bsq_version"]
 
 
 class BsqError(RuntimeError):
@@ -54,12 +54,14 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         L.bsq_packed_bytes.argtypes = [_c_int, _c_int, _i64, _i64, _sz, _sz, _sz]
         L.bsq_pack_host.argtypes = [_c_int, _c_int, _vp, _i64, _i64, _vp, _vp, _vp, ctypes.POINTER(_f32)]
-        L.bsq_quantize.argtypes = [_c_int, _c_int, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.bsq_quantize.argtypes = [_c_int, _c_int, _vp, _c_int, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.bsq_qgemm_mx.argtypes = [_c_int, _vp, _vp, _c_int, _vp, _vp, _i64, _i64, _i64, _vp, _c_int, _vp]
         L.bsq_dequant.argtypes = [_c_int, _c_int, _i64, _i64, _vp, _vp, _vp, _f32, _vp, _vp]
         L.bsq_qgemv.argtypes = [_c_int, _c_int, _i64, _i64, _vp, _vp, _vp, _f32, _vp, _c_int, _vp, _c_int, _vp]
         L.bsq_qgemm.argtypes = [_c_int, _c_int, _i64, _i64, _i64, _vp, _vp, _vp, _f32, _vp, _c_int, _vp, _c_int, _vp]
         L.bsq_qgemm_path.argtypes = [_c_int] + L.bsq_qgemm.argtypes
-        for f in ("bsq_packed_bytes", "bsq_pack_host", "bsq_quantize", "bsq_dequant", "bsq_qgemv", "bsq_qgemm", "bsq_qgemm_path"):
+        for f in ("bsq_packed_bytes", "bsq_pack_host", "bsq_quantize", "bsq_dequant", "bsq_qgemv", "bsq_qgemm", "bsq_qgemm_path",
+                  "bsq_qgemm_mx"):
             getattr(L, f).restype = _c_int
         for f in ("bsq_status_string", "bsq_last_error", "bsq_version"):
             getattr(L, f).restype = ctypes.c_char_p
@@ -81,8 +83,12 @@ def bsq_pack_host(fmt, block, w, n, k, codes, scales, biases, global_out):
     return lib().bsq_pack_host(fmt, block, w, n, k, codes, scales, biases, global_out)
 
 
-def bsq_quantize(fmt, block, w, n, k, codes, scales, biases, global_dev, status_dev, stream):
-    return lib().bsq_quantize(fmt, block, w, n, k, codes, scales, biases, global_dev, status_dev, stream)
+def bsq_quantize(fmt, block, w, wt, n, k, codes, scales, biases, global_dev, status_dev, stream):
+    return lib().bsq_quantize(fmt, block, w, wt, n, k, codes, scales, biases, global_dev, status_dev, stream)
+
+
+def bsq_qgemm_mx(xfmt, x_codes, x_scales, wfmt, w_codes, w_scales, m, n, k, out, ot, stream):
+    return lib().bsq_qgemm_mx(xfmt, x_codes, x_scales, wfmt, w_codes, w_scales, m, n, k, out, ot, stream)
 
 
 def bsq_dequant(fmt, block, n, k, codes, scales, biases, global_scale, out, stream):
@@ -181,8 +187,8 @@ def quantize(fmt, w: torch.Tensor, block: int = 0, check_finite: bool = True) ->
     """Pack a device f32 [n,k] weight on the GPU (bsq_quantize).  The nvfp4
     global scale is read back to the host (one synchronizing copy)."""
     f = _fmt(fmt)
-    if w.dtype != torch.float32 or not w.is_cuda or not w.is_contiguous():
-        raise ValueError("w must be a contiguous float32 CUDA tensor")
+    if w.dtype not in (torch.float32, torch.bfloat16) or not w.is_cuda or not w.is_contiguous():
+        raise ValueError("w must be a contiguous float32 or bfloat16 CUDA tensor")
     n, k = w.shape
     cb, sb, bb = packed_bytes(f, n, k, block)
     dev = w.device
@@ -191,12 +197,26 @@ def quantize(fmt, w: torch.Tensor, block: int = 0, check_finite: bool = True) ->
     biases = torch.empty(max(bb, 2), dtype=torch.uint8, device=dev)[:bb] if bb else None
     gdev = torch.ones(1, dtype=torch.float32, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
-    st = bsq_quantize(f, block, _ptr(w), n, k, _ptr(codes), _ptr(scales), _ptr(biases), _ptr(gdev),
+    st = bsq_quantize(f, block, _ptr(w), _DT[w.dtype], n, k, _ptr(codes), _ptr(scales), _ptr(biases), _ptr(gdev),
                       _ptr(status) if check_finite else None, _stream(dev))
     _check(st, "bsq_quantize")
     if check_finite and int(status.item()) != OK:
         raise BsqError(int(status.item()), "bsq_quantize (device)")
     return PackedWeight(f, n, k, codes, scales, biases, float(gdev.item()) if f == NVFP4 else 1.0)
+
+
+def qgemm_mx(xq: PackedWeight, w: PackedWeight, out: torch.Tensor | None = None, out_dtype=torch.bfloat16):
+    """out = dequant(xq) @ dequant(w)^T on the scaled matrix cores (bsq_qgemm_mx);
+    xq is an MX-packed [m,k] activation (bsq_quantize), w an MX-packed [n,k] weight."""
+    if xq.k != w.k:
+        raise ValueError(f"k mismatch: activations {xq.k}, weight {w.k}")
+    dev = w.codes.device
+    if out is None:
+        out = torch.empty((xq.n, w.n), dtype=out_dtype, device=dev)
+    st = bsq_qgemm_mx(xq.fmt, _ptr(xq.codes), _ptr(xq.scales), w.fmt, _ptr(w.codes), _ptr(w.scales), xq.n, w.n, w.k,
+                      _ptr(out), _DT[out.dtype], _stream(dev))
+    _check(st, "bsq_qgemm_mx")
+    return out
 
 
 def to_device(pw: PackedWeight, device="cuda") -> PackedWeight:

@@ -127,11 +127,12 @@ bsq_status bsq_pack_host(bsq_format fmt, int block, const float *w, int64_t n, i
   return ok();
 }
 
-bsq_status bsq_quantize(bsq_format fmt, int block, const float *w, int64_t n, int64_t k, void *codes, void *scales,
-                        void *biases, float *global_dev, int *status_dev, void *stream) {
+bsq_status bsq_quantize(bsq_format fmt, int block, const void *w, bsq_dtype wt, int64_t n, int64_t k, void *codes,
+                        void *scales, void *biases, float *global_dev, int *status_dev, void *stream) {
   bsq_status s;
   if ((s = check_format(fmt, block))) return s;
   if ((s = check_shape(fmt, n, k))) return s;
+  if (wt != BSQ_F32 && wt != BSQ_BF16) return fail(BSQ_ERR_ARG, "bad input dtype %d", (int)wt);
   if (n == 0 || k == 0) return ok();
   if (!w || !codes || !scales) return fail(BSQ_ERR_ARG, "null pointer");
   if (fmt == BSQ_INT4_AFFINE && !biases) return fail(BSQ_ERR_ARG, "int4 affine needs biases");
@@ -140,9 +141,30 @@ bsq_status bsq_quantize(bsq_format fmt, int block, const float *w, int64_t n, in
   if (!aligned(scales, scale_elem_bytes(fmt)) || (biases && !aligned(biases, 2)) ||
       (global_dev && !aligned(global_dev, 4)) || (status_dev && !aligned(status_dev, 4)))
     return fail(BSQ_ERR_ALIGN, "scales, biases, global or status misaligned");
-  return hip_status(bsq::launch_quantize(fmt, w, n, k, codes, scales, biases, global_dev, status_dev,
+  return hip_status(bsq::launch_quantize(fmt, w, (int)wt, n, k, codes, scales, biases, global_dev, status_dev,
                                          (hipStream_t)stream),
                     "quantize launch");
+}
+
+bsq_status bsq_qgemm_mx(bsq_format xfmt, const void *x_codes, const void *x_scales, bsq_format wfmt,
+                        const void *w_codes, const void *w_scales, int64_t m, int64_t n, int64_t k, void *out,
+                        bsq_dtype ot, void *stream) {
+  auto is_mx = [](int f) { return f == BSQ_MXFP4 || f == BSQ_MXFP8_E4M3 || f == BSQ_MXFP8_E5M2; };
+  if (!is_mx(xfmt) || !is_mx(wfmt)) return fail(BSQ_ERR_UNSUPPORTED, "both operands must be MX formats");
+  if (m < 0 || n < 0 || k < 0) return fail(BSQ_ERR_ARG, "negative size");
+  if (k % 128) return fail(BSQ_ERR_SHAPE, "k=%lld is not a multiple of 128", (long long)k);
+  if (ot != BSQ_F32 && ot != BSQ_BF16) return fail(BSQ_ERR_ARG, "bad out dtype %d", (int)ot);
+  if (m == 0 || n == 0) return ok();
+  if (!out) return fail(BSQ_ERR_ARG, "null out");
+  if (!aligned(out, ot == BSQ_F32 ? 4 : 2)) return fail(BSQ_ERR_ALIGN, "out misaligned");
+  hipStream_t st = (hipStream_t)stream;
+  if (k == 0) return hip_status(bsq::launch_zero(out, m * n * (ot == BSQ_F32 ? 4 : 2), st), "zero-fill");
+  if (m > ((int64_t)1 << 40) / k || n > ((int64_t)1 << 40) / k) return fail(BSQ_ERR_SHAPE, "sizes too large");
+  if (!x_codes || !x_scales || !w_codes || !w_scales) return fail(BSQ_ERR_ARG, "null pointer");
+  if (!aligned(x_codes, 16) || !aligned(w_codes, 16)) return fail(BSQ_ERR_ALIGN, "codes must be 16-byte aligned");
+  if (!aligned(x_scales, 2) || !aligned(w_scales, 2)) return fail(BSQ_ERR_ALIGN, "scales must be 2-byte aligned");
+  return hip_status(bsq::launch_mxmma(xfmt, x_codes, x_scales, wfmt, w_codes, w_scales, m, n, k, out, (int)ot, st),
+                    "mx mfma launch");
 }
 
 bsq_status bsq_dequant(bsq_format fmt, int block, int64_t n, int64_t k, const void *codes, const void *scales,

@@ -56,8 +56,12 @@ hipError_t launch_zero(void *out, int64_t bytes, hipStream_t s);
 // Device packer (quantize.hip): the host packer's encoding on the GPU.  gdev
 // (nvfp4) receives the global scale; status (may be null) receives 5 if a
 // block holds a non-finite value.
-hipError_t launch_quantize(int fmt, const float *w, int64_t n, int64_t k, void *codes, void *scales, void *biases,
-                           float *gdev, int *status, hipStream_t s);
+hipError_t launch_quantize(int fmt, const void *w, int wt, int64_t n, int64_t k, void *codes, void *scales,
+                           void *biases, float *gdev, int *status, hipStream_t s);
+// Scaled-MFMA GEMM (mxmma.hip): both operands MX-packed (mxfp4 / mxfp8),
+// k a multiple of 128.
+hipError_t launch_mxmma(int xfmt, const void *xc, const void *xs, int wfmt, const void *wc, const void *ws, int64_t m,
+                        int64_t n, int64_t k, void *out, int ot, hipStream_t s);
 
 // Host packer (pack_host.cpp).  Returns a bsq_status value.
 int pack_host(int fmt, const float *w, int64_t n, int64_t k, void *codes, void *scales, void *biases,

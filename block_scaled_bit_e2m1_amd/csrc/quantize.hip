@@ -1,4 +1,4 @@
-// quantize.hip -- device packer: f32 W [n,k] in HBM -> codes + block scales.
+// quantize.hip -- device packer: f32 or bf16 [n,k] in HBM -> codes + block scales.
 //
 // The same encoding as the host packer (pack_math.hpp: per-block scale from
 // the block amax, codes against the stored scale, fp64 quotients), computed on
@@ -21,11 +21,33 @@ __global__ void amax_init(float *g) {
   if (threadIdx.x == 0 && blockIdx.x == 0) *g = 0.0f;
 }
 
-__global__ void __launch_bounds__(256) amax_kernel(const float4 *__restrict__ w, int64_t n4, unsigned *__restrict__ g) {
+// Loads 8 consecutive inputs (f32 or bf16) as f32 values.
+template <int XT>
+__device__ __forceinline__ void load8(const void *base, int64_t idx, float x[8]) {
+  if constexpr (XT == 0) {
+    const float4 *p = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(base) + idx);
+    const float4 a = p[0], b = p[1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  } else {
+    const uint4 v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(base) + idx);
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(u[i] << 16);
+      x[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+    }
+  }
+}
+
+template <int XT>
+__global__ void __launch_bounds__(256) amax_kernel(const void *__restrict__ w, int64_t n8, unsigned *__restrict__ g) {
   float a = 0.0f;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
-    const float4 v = w[i];
-    a = fmaxf(a, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += (int64_t)gridDim.x * blockDim.x) {
+    float x[8];
+    load8<XT>(w, i * 8, x);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) a = fmaxf(a, fabsf(x[q]));
   }
   // wave-level max first: one atomic per wave
   for (int o = 32; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
@@ -36,9 +58,9 @@ __global__ void global_finalize(float *g) {
   if (threadIdx.x == 0 && blockIdx.x == 0) *g = pk::nvfp4_global(*g);
 }
 
-template <int F>
+template <int F, int XT>
 __global__ void __launch_bounds__(256)
-quantize_kernel(const float *__restrict__ w, int64_t n, int64_t k, const float *__restrict__ gdev,
+quantize_kernel(const void *__restrict__ w, int64_t n, int64_t k, const float *__restrict__ gdev,
                 uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, uint8_t *__restrict__ biases,
                 int *__restrict__ status) {
   constexpr int B = Traits<F>::kBlock;
@@ -46,16 +68,9 @@ quantize_kernel(const float *__restrict__ w, int64_t n, int64_t k, const float *
   const float g = (F == kNVFP4) ? *gdev : 1.0f;
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < blocks; t += (int64_t)gridDim.x * blockDim.x) {
     const int64_t j = t / nb, b = t - j * nb;
-    const float *src = w + j * k + b * B;
     float x[B];
 #pragma unroll
-    for (int i = 0; i < B; i += 4) {
-      const float4 v = *reinterpret_cast<const float4 *>(src + i);
-      x[i] = v.x;
-      x[i + 1] = v.y;
-      x[i + 2] = v.z;
-      x[i + 3] = v.w;
-    }
+    for (int i = 0; i < B; i += 8) load8<XT>(w, j * k + b * B + i, x + i);
     bool finite = true;
 #pragma unroll
     for (int i = 0; i < B; ++i) finite = finite && isfinite(x[i]);
@@ -103,38 +118,45 @@ quantize_kernel(const float *__restrict__ w, int64_t n, int64_t k, const float *
   }
 }
 
-template <int F>
-hipError_t run(const float *w, int64_t n, int64_t k, void *codes, void *scales, void *biases, float *gdev,
+template <int F, int XT>
+hipError_t run(const void *w, int64_t n, int64_t k, void *codes, void *scales, void *biases, float *gdev,
                int *status, hipStream_t s) {
   if constexpr (F == kNVFP4) {
     hipLaunchKernelGGL(amax_init, dim3(1), dim3(64), 0, s, gdev);
-    const int64_t n4 = n * k / 4;
-    int64_t blocks = (n4 + 255) / 256;
+    const int64_t n8 = n * k / 8;
+    int64_t blocks = (n8 + 255) / 256;
     if (blocks > 2048) blocks = 2048;
-    hipLaunchKernelGGL(amax_kernel, dim3((unsigned)blocks), dim3(256), 0, s, reinterpret_cast<const float4 *>(w), n4,
+    hipLaunchKernelGGL(amax_kernel<XT>, dim3((unsigned)blocks), dim3(256), 0, s, w, n8,
                        reinterpret_cast<unsigned *>(gdev));
     hipLaunchKernelGGL(global_finalize, dim3(1), dim3(64), 0, s, gdev);
   }
   const int64_t nblocks = n * (k / Traits<F>::kBlock);
   int64_t grid = (nblocks + 255) / 256;
   if (grid > 65536) grid = 65536;
-  hipLaunchKernelGGL(quantize_kernel<F>, dim3((unsigned)grid), dim3(256), 0, s, w, n, k, gdev, (uint8_t *)codes,
-                     (uint8_t *)scales, (uint8_t *)biases, status);
+  hipLaunchKernelGGL((quantize_kernel<F, XT>), dim3((unsigned)grid), dim3(256), 0, s, w, n, k, gdev,
+                     (uint8_t *)codes, (uint8_t *)scales, (uint8_t *)biases, status);
   return hipGetLastError();
+}
+
+template <int F>
+hipError_t run_t(const void *w, int wt, int64_t n, int64_t k, void *codes, void *scales, void *biases, float *gdev,
+                 int *status, hipStream_t s) {
+  return wt == 1 ? run<F, 1>(w, n, k, codes, scales, biases, gdev, status, s)
+                 : run<F, 0>(w, n, k, codes, scales, biases, gdev, status, s);
 }
 
 }  // namespace
 
-hipError_t launch_quantize(int fmt, const float *w, int64_t n, int64_t k, void *codes, void *scales, void *biases,
-                           float *gdev, int *status, hipStream_t s) {
+hipError_t launch_quantize(int fmt, const void *w, int wt, int64_t n, int64_t k, void *codes, void *scales,
+                           void *biases, float *gdev, int *status, hipStream_t s) {
   switch (fmt) {
-    case kMXFP4: return run<kMXFP4>(w, n, k, codes, scales, biases, gdev, status, s);
-    case kNVFP4: return run<kNVFP4>(w, n, k, codes, scales, biases, gdev, status, s);
-    case kMXFP8_E4M3: return run<kMXFP8_E4M3>(w, n, k, codes, scales, biases, gdev, status, s);
-    case kMXFP8_E5M2: return run<kMXFP8_E5M2>(w, n, k, codes, scales, biases, gdev, status, s);
-    case kNVFP8: return run<kNVFP8>(w, n, k, codes, scales, biases, gdev, status, s);
-    case kINT4_AFFINE: return run<kINT4_AFFINE>(w, n, k, codes, scales, biases, gdev, status, s);
-    case kINT8_SYM: return run<kINT8_SYM>(w, n, k, codes, scales, biases, gdev, status, s);
+    case kMXFP4: return run_t<kMXFP4>(w, wt, n, k, codes, scales, biases, gdev, status, s);
+    case kNVFP4: return run_t<kNVFP4>(w, wt, n, k, codes, scales, biases, gdev, status, s);
+    case kMXFP8_E4M3: return run_t<kMXFP8_E4M3>(w, wt, n, k, codes, scales, biases, gdev, status, s);
+    case kMXFP8_E5M2: return run_t<kMXFP8_E5M2>(w, wt, n, k, codes, scales, biases, gdev, status, s);
+    case kNVFP8: return run_t<kNVFP8>(w, wt, n, k, codes, scales, biases, gdev, status, s);
+    case kINT4_AFFINE: return run_t<kINT4_AFFINE>(w, wt, n, k, codes, scales, biases, gdev, status, s);
+    case kINT8_SYM: return run_t<kINT8_SYM>(w, wt, n, k, codes, scales, biases, gdev, status, s);
   }
   return hipErrorInvalidValue;
 }

@@ -101,19 +101,34 @@ bsq_status bsq_packed_bytes(bsq_format fmt, int block, int64_t n, int64_t k, siz
 bsq_status bsq_pack_host(bsq_format fmt, int block, const float *w, int64_t n, int64_t k, void *codes,
                          void *scales, void *biases, float *global_out);
 
-/* Device packer: the same encoding as bsq_pack_host (byte-identical output),
- * computed on the GPU from a weight already in HBM -- the quantize producer
- * of the pages' scaled-matmul ops [rlx-cpu quant.rs, lowp_compute_scales /
- * lowp_quantize; metaltile PR #250, QFormat pack commit].
- * w: device f32 [n,k], 16-byte aligned.  codes/scales/biases: device buffers
+/* Device packer: the same encoding as bsq_pack_host (byte-identical output
+ * for f32 input), computed on the GPU from a tensor already in HBM -- the
+ * quantize producer of the pages' scaled-matmul ops [rlx-cpu quant.rs,
+ * lowp_compute_scales / lowp_quantize; metaltile PR #250, QFormat pack
+ * commit].  Used for weights and, with an MX format, for activations.
+ * w: device [n,k] of dtype wt (f32, or bf16 whose values are converted to f32
+ * exactly), 16-byte aligned.  codes/scales/biases: device buffers
  * sized by bsq_packed_bytes (biases for int4 only).  global_dev: device float,
  * required for nvfp4 (receives f32(T/2688) computed from the tensor amax T on
  * the device; the caller reads it back if it needs it on the host), ignored
  * otherwise.  status_dev: optional device int that the kernel sets to
  * BSQ_ERR_NONFINITE if any weight is NaN or inf (that block's bytes are then
  * unspecified); the caller initialises it.  Asynchronous on `stream`. */
-bsq_status bsq_quantize(bsq_format fmt, int block, const float *w, int64_t n, int64_t k, void *codes, void *scales,
-                        void *biases, float *global_dev, int *status_dev, void *stream);
+bsq_status bsq_quantize(bsq_format fmt, int block, const void *w, bsq_dtype wt, int64_t n, int64_t k, void *codes,
+                        void *scales, void *biases, float *global_dev, int *status_dev, void *stream);
+
+/* Both-operands block-scaled GEMM on the scaled matrix cores:
+ *   out[i,j] = sum_p dequant(Xq)[i,p] * dequant(W)[j,p]
+ * where Xq (activations, [m,k]) and W ([n,k]) are both packed in an MX format
+ * (BSQ_MXFP4, BSQ_MXFP8_E4M3 or BSQ_MXFP8_E5M2: E8M0 scale per 32 along k,
+ * stored layouts as above); per block acc += (a_scale * b_scale) *
+ * sum dec(a) * dec(b) in fp32 [rlx-cpu quant.rs, lowp_scaled_matmul].  This is
+ * an activation-quantized contract: X is first packed with bsq_quantize.
+ * k must be a multiple of 128 (BSQ_ERR_SHAPE otherwise); codes 16-byte
+ * aligned, scales 2-byte aligned.  out: device [m,n], f32 or bf16 (RNE). */
+bsq_status bsq_qgemm_mx(bsq_format xfmt, const void *x_codes, const void *x_scales, bsq_format wfmt,
+                        const void *w_codes, const void *w_scales, int64_t m, int64_t n, int64_t k, void *out,
+                        bsq_dtype ot, void *stream);
 
 /* Standalone dequant: out (device f32 [n,k]) = decode(code) * scale with one
  * rounding to f32 (nvfp4: (e2m1 * e4m3) * global; int4: s*q + b)

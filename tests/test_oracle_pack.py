@@ -341,3 +341,21 @@ def test_matmul_rejects_bad_rows(orc):
     x = np.zeros((2, 4), np.float32)
     with pytest.raises(orc.OracleError):
         orc.matmul(x, np.zeros((3, 4), np.float32), rows=[2])
+
+
+@pytest.mark.parametrize("xfmt,wfmt", [("mxfp8_e4m3", "mxfp4"), ("mxfp4", "mxfp4"), ("mxfp8_e5m2", "mxfp8_e4m3")])
+def test_scaled_matmul_block_factorization(orc, xfmt, wfmt):
+    """Both operands MX-packed: the oracle's dequant-then-dot equals the
+    per-block form acc += (a_scale * b_scale) * sum dec(a) * dec(b) of the
+    pages' TN scaled matmul, computed here from independent decode tables."""
+    m, n, k = 5, 7, 256
+    X = workloads.random_activations(m, k, seed=3, act="f32")
+    W = workloads.random_weights(n, k, seed=4, sigma=0.02, outliers=True)
+    px, pw = orc.pack(xfmt, X), orc.pack(wfmt, W)
+    ref, _ = orc.matmul(orc.dequant_packed(px), orc.dequant_packed(pw))
+    ca, cb = codes_of(xfmt, px).reshape(m, k // 32, 32), codes_of(wfmt, pw).reshape(n, k // 32, 32)
+    da, db = elem_table(xfmt)[ca], elem_table(wfmt)[cb]
+    sa, sb = scales_f64(xfmt, px), scales_f64(wfmt, pw)  # [m, k/32], [n, k/32]
+    blk = np.einsum("mbp,nbp->mnb", da, db)
+    want = np.einsum("mnb,mb,nb->mn", blk, sa, sb)
+    assert np.allclose(ref, want, rtol=1e-12, atol=1e-300)
