@@ -32,6 +32,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
+MFMA_FP8_PEAK_TFLOPS = 5000.0   # dense fp8 (an fp8 operand on either side of the scaled MFMA)
+MFMA_FP4_PEAK_TFLOPS = 10100.0  # dense fp4 (both operands fp4)
 ROTATE_BYTES = 640 << 20        # distinct weight copies per rotation (> 2x the 256 MB MALL)
 
 KERNEL_SOURCES = {"qgemv": "block_scaled_bit_e2m1_amd/csrc/rows.hip",
@@ -177,6 +179,69 @@ def time_quantize(device, fmt="mxfp4", n=4096, k=4096, launches=200):
             "roofline_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def graph_event_ms(fn, per_graph, reps, device):
+    """Average time (ms) of one fn() call: per_graph calls captured in a HIP
+    graph, replayed reps times, timed by events on the capture stream."""
+    import torch
+
+    stream = torch.cuda.Stream(device)
+    torch.cuda.synchronize(device)
+    with torch.cuda.stream(stream):
+        for _ in range(per_graph):
+            fn()
+    torch.cuda.synchronize(device)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(per_graph):
+            fn()
+    with torch.cuda.stream(stream):
+        g.replay()
+    torch.cuda.synchronize(device)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize(device)
+    return e0.elapsed_time(e1) / (reps * per_graph)
+
+
+def time_qgemm_mx(device, xfmt, wfmt, m=2048, n=4096, k=4096, reps=100):
+    """Both-operands MX GEMM on the scaled MFMA (bsq_qgemm_mx), bf16 out:
+    the GEMM alone, and with the device quantize of the bf16 activations in
+    front of it (the activation-quantized step as a caller runs it)."""
+    import torch
+
+    from block_scaled_bit_e2m1_amd import bsq, workloads
+
+    w = bsq.to_device(bsq.pack(wfmt, workloads.random_weights(n, k, seed=1003, sigma=0.02)), device)
+    x = torch.from_numpy(workloads.random_activations(m, k, seed=1004, act="bf16")).to(torch.bfloat16).to(device)
+    xq = bsq.quantize(xfmt, x)
+    out = torch.empty((m, n), dtype=torch.bfloat16, device=device)
+    gdev = torch.ones(1, dtype=torch.float32, device=device)
+    status = torch.zeros(1, dtype=torch.int32, device=device)
+
+    def gemm():
+        bsq.qgemm_mx(xq, w, out=out)
+
+    def step():
+        st = bsq.bsq_quantize(xq.fmt, 0, bsq._ptr(x), bsq.BF16, m, k, bsq._ptr(xq.codes), bsq._ptr(xq.scales), None,
+                              bsq._ptr(gdev), bsq._ptr(status), bsq._stream(device))
+        assert st == bsq.OK
+        gemm()
+
+    flops = 2.0 * m * n * k
+    peak = MFMA_FP4_PEAK_TFLOPS if xfmt == wfmt == "mxfp4" else MFMA_FP8_PEAK_TFLOPS
+    g_ms = graph_event_ms(gemm, 4, reps, device)
+    s_ms = graph_event_ms(step, 4, reps // 2, device)
+    tf = flops / (g_ms * 1e-3) / 1e12
+    return {"workload": f"qgemm_mx_{xfmt}_x_{wfmt}_{m}x{n}x{k}",
+            "note": "scaled-MFMA GEMM, X and W both MX-packed (bsq_qgemm_mx), bf16 out; step = X quantize + GEMM",
+            "value": round(tf, 2), "unit": "TFLOP/s", "us_per_launch": round(g_ms * 1e3, 3),
+            "peak": peak, "roofline_frac": round(tf / peak, 4), "us_per_step_with_x_quantize": round(s_ms * 1e3, 3)}
+
+
 def cpu_baseline(wl, budget_s=10.0):
     """The oracle as it stands (dequant, then fp64 dot) on the host cores."""
     import numpy as np
@@ -219,6 +284,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only-timed", action="store_true", help="timed workload only (for profiling)")
+    ap.add_argument("--mx-only", action="store_true", help="only time the scaled-MFMA GEMMs and exit")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="only run torch's copy kernel on MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -244,6 +310,10 @@ def main():
         print(json.dumps({"calib_copy_bytes": n, "launches": max(1, args.steps)}), flush=True)
         return
     bsq.lib()
+    if args.mx_only:
+        for xf, wf in [("mxfp4", "mxfp4"), ("mxfp8_e4m3", "mxfp4"), ("mxfp8_e4m3", "mxfp8_e4m3")]:
+            print(json.dumps(time_qgemm_mx(device, xf, wf)), flush=True)
+        return
     wl = workloads.WORKLOADS[args.workload]
     kind = "qgemv" if wl.op == "qgemv" else "qgemm"
     log(f"bench: {wl.name} steps={args.steps} warmup={args.warmup}")
@@ -296,6 +366,11 @@ def main():
 
     if not args.no_extra and not args.only_timed:
         extra.append(time_quantize(device))
+        for xf, wf in [("mxfp4", "mxfp4"), ("mxfp8_e4m3", "mxfp4"), ("mxfp8_e4m3", "mxfp8_e4m3")]:
+            e = time_qgemm_mx(device, xf, wf)
+            extra.append(e)
+            log(f"  {e['workload']}: {e['value']:.1f} TFLOP/s ({e['us_per_launch']:.2f} us/launch, "
+                f"{e['us_per_step_with_x_quantize']:.2f} us with X quantize)")
 
     cpu = None
     if not args.no_cpu and not args.only_timed:

@@ -33,6 +33,9 @@ namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+// Slot data as a native vector (HIP's uint4 struct is copied with memcpy and
+// kept in scratch memory).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int BKX = 128;          // k per step
 constexpr int LDX = BKX + 16;     // bytes per LDS row of the X code tile (8-bit codes)
@@ -47,7 +50,7 @@ template <> struct MxFmt<kMXFP4> { static constexpr int kCode = 4, kBits = 4; };
 // pieces for 8-bit) and the E8M0 scale bytes of blocks 2h and 2h+1.
 template <int FB>
 struct WSlot {
-  uint4 c[MxFmt<FB>::kBits / 2];  // 2 (4-bit) or 4 (8-bit) x 16 bytes
+  u32x4_t c[MxFmt<FB>::kBits / 2];  // 2 (4-bit) or 4 (8-bit) x 16 bytes
   uint32_t s;                     // two scale bytes (low byte: first 32-block)
 };
 
@@ -112,34 +115,34 @@ mxmma_kernel(const uint8_t *__restrict__ xc, const uint8_t *__restrict__ xsc, co
 
   const int KT = (int)(k / BKX);
   struct Slot {
-    uint4 x[XCH];
+    u32x4_t x[XCH];
     WSlot<FB> w[NT];
     uint32_t xs2[MT];  // X scale byte pairs of this lane's rows
   };
   Slot G[D];
 
-  auto load = [&](Slot &g, int kt) {
+  auto load = [&](Slot &g, int kt) __attribute__((always_inline)) {
     const int64_t k0 = (int64_t)kt * BKX;
 #pragma unroll
-    for (int c = 0; c < XCH; ++c) g.x[c] = *reinterpret_cast<const uint4 *>(xp[c] + k0 * ABITS / 8);
+    for (int c = 0; c < XCH; ++c) g.x[c] = *reinterpret_cast<const u32x4_t *>(xp[c] + k0 * ABITS / 8);
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
 #pragma unroll
       for (int q = 0; q < BBITS / 2; ++q)
-        g.w[j].c[q] = *reinterpret_cast<const uint4 *>(wp[j] + k0 * BBITS / 8 + (BBITS == 4 ? 16 : 32) * q);
+        g.w[j].c[q] = *reinterpret_cast<const u32x4_t *>(wp[j] + k0 * BBITS / 8 + (BBITS == 4 ? 16 : 32) * q);
       g.w[j].s = *reinterpret_cast<const uint16_t *>(wsp[j] + k0 / 32);
     }
 #pragma unroll
     for (int i = 0; i < MT; ++i) g.xs2[i] = *reinterpret_cast<const uint16_t *>(xsp[i] + k0 / 32);
   };
-  auto store_x = [&](const Slot &g, int buf) {
+  auto store_x = [&](const Slot &g, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < XCH; ++c) {
       const int cid = c * NTHR + tid;
-      *reinterpret_cast<uint4 *>(&xs[buf][(cid / CPR) * LDX + (cid % CPR) * 16]) = g.x[c];
+      *reinterpret_cast<u32x4_t *>(&xs[buf][(cid / CPR) * LDX + (cid % CPR) * 16]) = g.x[c];
     }
   };
-  auto step = [&](auto guard, int kt, Slot &cur, const Slot &nxt) {
+  auto step = [&](auto guard, int kt, Slot &cur, const Slot &nxt) __attribute__((always_inline)) {
     constexpr bool kGuard = decltype(guard)::value;
     const uint8_t *xb = xs[kt & 1];
     // A operands of both slices: 16 (4-bit) or 2 x 16 (8-bit) bytes per lane each
@@ -149,8 +152,8 @@ mxmma_kernel(const uint8_t *__restrict__ xc, const uint8_t *__restrict__ xsc, co
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
         const uint8_t *row = &xb[(wm * WTM + i * 32 + l32) * LDX];
-        const uint4 lo = *reinterpret_cast<const uint4 *>(row + (ABITS == 4 ? 32 * h + 16 * s : 16 * h + 32 * s));
-        const uint4 hi = ABITS == 8 ? *reinterpret_cast<const uint4 *>(row + 64 + 16 * h + 32 * s) : make_uint4(0, 0, 0, 0);
+        const u32x4_t lo = *reinterpret_cast<const u32x4_t *>(row + (ABITS == 4 ? 32 * h + 16 * s : 16 * h + 32 * s));
+        const u32x4_t hi = ABITS == 8 ? *reinterpret_cast<const u32x4_t *>(row + 64 + 16 * h + 32 * s) : u32x4_t{0, 0, 0, 0};
         a[s][i] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
     i32x8_t b[2][NT];
@@ -161,10 +164,10 @@ mxmma_kernel(const uint8_t *__restrict__ xc, const uint8_t *__restrict__ xsc, co
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         if constexpr (BBITS == 4) {
-          const uint4 c = cur.w[j].c[s];
+          const u32x4_t c = cur.w[j].c[s];
           b[s][j] = i32x8_t{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
         } else {
-          const uint4 c0 = cur.w[j].c[s], c1 = cur.w[j].c[2 + s];
+          const u32x4_t c0 = cur.w[j].c[s], c1 = cur.w[j].c[2 + s];
           b[s][j] = i32x8_t{(int)c0.x, (int)c0.y, (int)c0.z, (int)c0.w, (int)c1.x, (int)c1.y, (int)c1.z, (int)c1.w};
         }
       }
