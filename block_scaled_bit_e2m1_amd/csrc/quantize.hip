@@ -6,11 +6,21 @@
 // [rlx-cpu quant.rs, lowp_compute_scales and lowp_quantize, which the pages
 // run as producer ops of the scaled matmul].
 //
-// One thread packs one block: it reads the block's B floats (16-byte loads,
-// adjacent threads on adjacent blocks), encodes, and writes the block's codes
-// (B/2 or B bytes) and its scale.  nvfp4 first reduces the tensor amax into
-// the caller's device float (vector atomicMax on the bits of non-negative
-// floats), then turns it into the global scale in place.
+// MX formats (the activation formats of the scaled-MFMA GEMM): a lane owns 8
+// consecutive elements, so one 32-block is a quad of lanes and every load is a
+// coalesced 16- or 32-byte run.  The quad's amax (two lane swaps) gives the
+// E8M0 byte; each element is then scaled by 2^(127-b) in f32, which is the
+// exact quotient whenever the result is a normal f32 (results below 2^-126 lie
+// under every format's smallest rounding threshold, so they encode to a signed
+// zero either way), and rounded onto the minifloat grid by a power-of-two
+// rescale and rintf (nearest, ties to even): the same codes as the fp64
+// encoder, with no fp64 arithmetic.
+//
+// Other formats: one thread packs one block with the fp64 encoder (their
+// scales are not powers of two, so the quotient needs the wider type).
+// nvfp4 first reduces the tensor amax into the caller's device float (vector
+// atomicMax on the bits of non-negative floats), then turns it into the
+// global scale in place.
 #include "bsq_internal.hpp"
 #include "pack_math.hpp"
 
@@ -56,6 +66,80 @@ __global__ void __launch_bounds__(256) amax_kernel(const void *__restrict__ w, i
 
 __global__ void global_finalize(float *g) {
   if (threadIdx.x == 0 && blockIdx.x == 0) *g = pk::nvfp4_global(*g);
+}
+
+// Nearest-even code of a finite a >= 0 on a minifloat grid with M mantissa
+// bits and exponent bias BT (subnormals included), clamped to MAXC.  a * 2^-qe
+// is exact (a power-of-two rescale of an f32 that neither overflows nor
+// underflows), so rintf decides the rounding exactly.
+template <int M, int BT, int MAXC>
+__device__ __forceinline__ uint32_t grid_code(float a) {
+  if (!(a > 0.0f)) return 0u;
+  int ex;
+  frexpf(a, &ex);  // a in [2^(ex-1), 2^ex)
+  const int e = ex - 1, emin = 1 - BT;
+  const int qe = (e < emin ? emin : e) - M;
+  const int q = (int)rintf(ldexpf(a, -qe));
+  const int code = e < emin ? q : ((e + BT) << M) + q - (1 << M);
+  return (uint32_t)(code < MAXC ? code : MAXC);
+}
+
+template <int F> struct MxEnc;
+template <> struct MxEnc<kMXFP4> {
+  static constexpr int kEmax = 2;
+  __device__ static uint32_t enc(float v) { return grid_code<1, 1, 7>(fabsf(v)) | (signbit(v) ? 8u : 0u); }
+};
+template <> struct MxEnc<kMXFP8_E4M3> {
+  static constexpr int kEmax = 8;
+  __device__ static uint32_t enc(float v) { return grid_code<3, 7, 0x7E>(fabsf(v)) | (signbit(v) ? 0x80u : 0u); }
+};
+template <> struct MxEnc<kMXFP8_E5M2> {
+  static constexpr int kEmax = 15;
+  __device__ static uint32_t enc(float v) { return grid_code<2, 15, 0x7B>(fabsf(v)) | (signbit(v) ? 0x80u : 0u); }
+};
+
+template <int F, int XT>
+__global__ void __launch_bounds__(256)
+quantize_mx_kernel(const void *__restrict__ w, int64_t n8, uint8_t *__restrict__ codes,
+                   uint8_t *__restrict__ scales, int *__restrict__ status) {
+  // n8 (elements / 8) is a multiple of 4, so a quad is always wholly inside
+  // or outside the range and the lane swaps read active lanes only.
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n8; t += (int64_t)gridDim.x * blockDim.x) {
+    float x[8];
+    load8<XT>(w, t * 8, x);
+    float a = 0.0f;
+    bool finite = true;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      finite = finite && isfinite(x[i]);
+      a = fmaxf(a, fabsf(x[i]));
+    }
+    a = fmaxf(a, __shfl_xor(a, 1));
+    a = fmaxf(a, __shfl_xor(a, 2));
+    if (!finite && status) *status = 5;  // BSQ_ERR_NONFINITE; the block's bytes are then unspecified
+    int sb = 127;
+    if (a > 0.0f) {
+      int ex;
+      frexpf(a, &ex);
+      int e = ex - 1 - MxEnc<F>::kEmax;
+      e = e < -127 ? -127 : (e > 127 ? 127 : e);
+      sb = e + 127;
+    }
+    uint32_t c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = MxEnc<F>::enc(ldexpf(x[i], 127 - sb));
+    if constexpr (F == kMXFP4) {
+      uint32_t wd = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) wd |= c[i] << (4 * i);
+      reinterpret_cast<uint32_t *>(codes)[t] = wd;
+    } else {
+      const uint32_t lo = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+      const uint32_t hi = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+      reinterpret_cast<uint2 *>(codes)[t] = make_uint2(lo, hi);
+    }
+    if ((t & 3) == 0) scales[t >> 2] = (uint8_t)sb;
+  }
 }
 
 template <int F, int XT>
@@ -129,6 +213,15 @@ hipError_t run(const void *w, int64_t n, int64_t k, void *codes, void *scales, v
     hipLaunchKernelGGL(amax_kernel<XT>, dim3((unsigned)blocks), dim3(256), 0, s, w, n8,
                        reinterpret_cast<unsigned *>(gdev));
     hipLaunchKernelGGL(global_finalize, dim3(1), dim3(64), 0, s, gdev);
+  }
+  if constexpr (F == kMXFP4 || F == kMXFP8_E4M3 || F == kMXFP8_E5M2) {
+    const int64_t n8 = n * k / 8;
+    int64_t grid = (n8 + 255) / 256;
+    if (grid > 65536) grid = 65536;
+    if (grid > 0)
+      hipLaunchKernelGGL((quantize_mx_kernel<F, XT>), dim3((unsigned)grid), dim3(256), 0, s, w, n8, (uint8_t *)codes,
+                         (uint8_t *)scales, status);
+    return hipGetLastError();
   }
   const int64_t nblocks = n * (k / Traits<F>::kBlock);
   int64_t grid = (nblocks + 255) / 256;
