@@ -162,7 +162,7 @@ bsq_status bsq_qgemm_mx(bsq_format xfmt, const void *x_codes, const void *x_scal
   if (m > ((int64_t)1 << 40) / k || n > ((int64_t)1 << 40) / k) return fail(BSQ_ERR_SHAPE, "sizes too large");
   if (!x_codes || !x_scales || !w_codes || !w_scales) return fail(BSQ_ERR_ARG, "null pointer");
   if (!aligned(x_codes, 16) || !aligned(w_codes, 16)) return fail(BSQ_ERR_ALIGN, "codes must be 16-byte aligned");
-  if (!aligned(x_scales, 2) || !aligned(w_scales, 2)) return fail(BSQ_ERR_ALIGN, "scales must be 2-byte aligned");
+  if (!aligned(x_scales, 4) || !aligned(w_scales, 4)) return fail(BSQ_ERR_ALIGN, "scales must be 4-byte aligned");
   return hip_status(bsq::launch_mxmma(xfmt, x_codes, x_scales, wfmt, w_codes, w_scales, m, n, k, out, (int)ot, st),
                     "mx mfma launch");
 }

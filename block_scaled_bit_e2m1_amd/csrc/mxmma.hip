@@ -11,18 +11,28 @@
 // holds [16h, 16h+16) in its bytes 0..15 and [32+16h, 48+16h) in bytes 16..31
 // (both read off the instruction with one-hot inputs).
 //
-// Geometry (CDNA4, wave64): workgroup tile 256x128, 2x2 waves (wave tile
-// 128x64), k step 128 = four 32-blocks = two MFMA slices.  Slice s puts
-// logical block 2j+s in hardware block j, for both operands and either width,
-// so lane half h always owns the scale pair of blocks 2h, 2h+1 (one 16-bit
-// load, byte s selected by opsel) and the k orders of mixed-width pairs agree:
-// 4-bit lanes read the 64 contiguous codes of blocks 2h, 2h+1 (32 bytes),
-// 8-bit lanes the 16-byte pieces at 16h + 32q, q = 0..3 (slice s uses q = s
-// and q = 2+s).  W codes go straight from HBM into B-operand registers; X
-// codes are staged through LDS (double buffered, rows padded to 144 B) and
-// their scales loaded like W's.  Two-deep register prefetch, branch-free
-// steady state (4 steps per loop trip), XCD-aware tile order, as in the bf16
-// MFMA kernel.
+// k order.  A step covers 128 k = four 32-blocks = two MFMA slices; slice s
+// puts logical block 2j+s in hardware block j, for both operands and either
+// width, so lane half h always needs the scale bytes of blocks 2h and 2h+1
+// (byte s selected by opsel) and the k orders of mixed-width pairs agree.
+// In 16-byte chunks of a row's 64 (4-bit) or 128 (8-bit) code bytes per step,
+// a 4-bit lane reads chunk 2h+s, an 8-bit lane chunks h+2s and 4+h+2s.
+//
+// Data movement.  Partial-line global loads leave the kernel bound by L1
+// accesses, so every global load reads whole contiguous runs: both code tiles
+// go through LDS (consecutive threads on consecutive 16-byte chunks of a row),
+// written with the chunk index XOR-swizzled by row so that the row writes and
+// the per-lane operand reads are both free of bank conflicts.  Scales are
+// loaded once per 4 steps (16 bytes per row; four lanes per row, so their
+// dword loads coalesce into one access), staged in LDS and read as one dword
+// per row per step.  Codes are prefetched D steps ahead in registers, scales
+// one 4-step trip ahead; the steady loop is branch-free and the ragged end is
+// a guarded drain.
+//
+// Geometry (CDNA4, wave64): workgroup tile 256x128 (128x64 for small
+// problems), 2x2 waves, fp32 accumulators in AGPRs.  Tiles are renumbered so
+// each XCD (own L2) runs a block of GM m-tiles by consecutive n-tiles, which
+// bounds the W and X bytes one L2 must hold.
 #include "bsq_internal.hpp"
 #include "codec.hpp"
 
@@ -33,12 +43,12 @@ namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
-// Slot data as a native vector (HIP's uint4 struct is copied with memcpy and
-// kept in scratch memory).
+// Register staging as native vectors (HIP's uint4 struct is copied with memcpy
+// and kept in scratch memory).
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int BKX = 128;          // k per step
-constexpr int LDX = BKX + 16;     // bytes per LDS row of the X code tile (8-bit codes)
+constexpr int BK = 128;  // k per step
+constexpr int TRIP = 4;  // steps per scale load: 16 scale bytes per row
 
 // scaled-MFMA operand format codes
 template <int F> struct MxFmt;
@@ -46,15 +56,18 @@ template <> struct MxFmt<kMXFP8_E4M3> { static constexpr int kCode = 0, kBits = 
 template <> struct MxFmt<kMXFP8_E5M2> { static constexpr int kCode = 1, kBits = 8; };
 template <> struct MxFmt<kMXFP4> { static constexpr int kCode = 4, kBits = 4; };
 
-// One lane's data for one step: its codes (32 bytes for 4-bit, four 16-byte
-// pieces for 8-bit) and the E8M0 scale bytes of blocks 2h and 2h+1.
-template <int FB>
-struct WSlot {
-  u32x4_t c[MxFmt<FB>::kBits / 2];  // 2 (4-bit) or 4 (8-bit) x 16 bytes
-  uint32_t s;                     // two scale bytes (low byte: first 32-block)
+// LDS tile with RB-byte rows: byte offset of 16-byte chunk c of row r.  The
+// chunk index is XORed with a key of the row so that 16 consecutive rows at
+// one chunk, and the chunks of consecutive rows, fall on distinct banks
+// (64 banks x 4 bytes = 256 bytes per pass).
+template <int RB> struct Swz {
+  static constexpr int kCPR = RB / 16, kRPB = 256 / RB;
+  static constexpr int kPeriod = kCPR * kRPB;  // rows after which the key repeats
+  __device__ static int key(int r) { return (r / kRPB) % kCPR; }
+  __device__ static int at(int r, int c) { return r * RB + ((c ^ key(r)) << 4); }
 };
 
-template <int FA, int FB, int BM, int BN, int WGM, int WGN, int D, int UK>
+template <int FA, int FB, int BM, int BN, int WGM, int WGN, int D, int GM>
 __global__ void __launch_bounds__(WGM *WGN * 64)
 mxmma_kernel(const uint8_t *__restrict__ xc, const uint8_t *__restrict__ xsc, const uint8_t *__restrict__ wc,
              const uint8_t *__restrict__ wsc, void *__restrict__ out, int ot, int64_t m, int64_t n, int64_t k,
@@ -63,16 +76,31 @@ mxmma_kernel(const uint8_t *__restrict__ xc, const uint8_t *__restrict__ xsc, co
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int MT = WTM / 32, NT = WTN / 32;
   constexpr int ABITS = MxFmt<FA>::kBits, BBITS = MxFmt<FB>::kBits;
-  constexpr int XROW = BKX * ABITS / 8;          // bytes of X codes per row per step (128 or 64)
-  constexpr int XCH = BM * (XROW / 16) / NTHR;   // 16-byte X chunks per thread per step
-  constexpr int CPR = XROW / 16;                 // chunks per row
-  static_assert(XCH * NTHR == BM * CPR, "X tile must split evenly");
-  __shared__ __attribute__((aligned(16))) uint8_t xs[2][BM * LDX];
+  constexpr int XR = BK * ABITS / 8, WR = BK * BBITS / 8;  // code bytes per row per step
+  constexpr int XCPR = XR / 16, WCPR = WR / 16;            // 16-byte chunks per row
+  constexpr int XCH = BM * XCPR / NTHR, WCH = BN * WCPR / NTHR;
+  constexpr int XRS = NTHR / XCPR, WRS = NTHR / WCPR;      // rows between a thread's chunks
+  constexpr int SCH = TRIP * (BM + BN) / NTHR;             // scale dwords per thread per trip
+  constexpr int SCX = TRIP * BM / NTHR;                    // ... of which on X rows
+  static_assert(XCH * NTHR == BM * XCPR && WCH * NTHR == BN * WCPR, "code tiles must split evenly");
+  static_assert(SCH * NTHR == TRIP * (BM + BN) && SCX * NTHR == TRIP * BM, "scale tile must split evenly");
+  static_assert(XRS % Swz<XR>::kPeriod == 0 && WRS % Swz<WR>::kPeriod == 0, "one swizzle key per thread");
+  static_assert(WTM % Swz<XR>::kPeriod == 0 && WTN % Swz<WR>::kPeriod == 0 && 32 % Swz<XR>::kPeriod == 0 &&
+                    32 % Swz<WR>::kPeriod == 0,
+                "one swizzle key per lane");
+  static_assert(TRIP % D == 0, "the prefetch ring must divide a trip");
+  __shared__ __attribute__((aligned(16))) uint8_t xs[2][BM * XR];
+  __shared__ __attribute__((aligned(16))) uint8_t ws[2][BN * WR];
+  __shared__ uint32_t ss[2][(BM + BN) * TRIP];
 
+  // tile order: XCD x runs tiles [x*T/8, (x+1)*T/8) (blocks are dealt to the
+  // XCDs round-robin), walked as GM m-tiles by consecutive n-tiles
   const int T = tiles_m * tiles_n;
   int t = blockIdx.x;
   if ((T & 7) == 0) t = (t & 7) * (T >> 3) + (t >> 3);
-  const int tm = t / tiles_n, tn = t - tm * tiles_n;
+  const int grp = t / (GM * tiles_n), tin = t - grp * (GM * tiles_n);
+  const int gm = min(GM, tiles_m - grp * GM);
+  const int tm = grp * GM + tin % gm, tn = tin / gm;
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -80,30 +108,46 @@ mxmma_kernel(const uint8_t *__restrict__ xc, const uint8_t *__restrict__ xsc, co
   const int l32 = lane & 31, h = lane >> 5;
   const int64_t nblk = k / 32;
   const int64_t xrb = k * ABITS / 8, wrb = k * BBITS / 8;  // code bytes per row
+  const int KT = (int)(k / BK);
 
+  // global sources of this thread's code chunks (rows past m or n read a
+  // valid row and are never stored) and their LDS destinations
   const uint8_t *xp[XCH];
+  const uint8_t *wp[WCH];
+  const int xr0 = tid / XCPR, xc0 = tid % XCPR, wr0 = tid / WCPR, wc0 = tid % WCPR;
 #pragma unroll
   for (int c = 0; c < XCH; ++c) {
-    const int cid = c * NTHR + tid;
-    const int64_t gr = m0 + cid / CPR;
-    xp[c] = xc + (gr < m ? gr : m - 1) * xrb + (cid % CPR) * 16;  // rows past m: valid, never stored
+    const int64_t gr = m0 + xr0 + c * XRS;
+    xp[c] = xc + (gr < m ? gr : m - 1) * xrb + xc0 * 16;
   }
-  const uint8_t *wp[NT];
-  const uint8_t *wsp[NT];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    int64_t gc = n0 + wn * WTN + j * 32 + l32;
-    gc = gc < n ? gc : n - 1;
-    wp[j] = wc + gc * wrb + (BBITS == 4 ? 32 : 16) * h;
-    wsp[j] = wsc + gc * nblk + 2 * h;
+  for (int c = 0; c < WCH; ++c) {
+    const int64_t gr = n0 + wr0 + c * WRS;
+    wp[c] = wc + (gr < n ? gr : n - 1) * wrb + wc0 * 16;
   }
-  const uint8_t *xsp[MT];
+  const int xd = Swz<XR>::at(xr0, xc0), wd = Swz<WR>::at(wr0, wc0);
+  // scale dwords: item q = c*NTHR + tid is row q/TRIP (X rows, then W rows), step q%TRIP of a trip
+  const uint8_t *sp[SCH];
+  const int sst = tid % TRIP;
 #pragma unroll
-  for (int i = 0; i < MT; ++i) {
-    int64_t gr = m0 + wm * WTM + i * 32 + l32;
-    gr = gr < m ? gr : m - 1;
-    xsp[i] = xsc + gr * nblk + 2 * h;
+  for (int c = 0; c < SCH; ++c) {
+    const int r = (c * NTHR + tid) / TRIP;
+    if (c < SCX) {
+      const int64_t gr = m0 + r;
+      sp[c] = xsc + (gr < m ? gr : m - 1) * nblk;
+    } else {
+      const int64_t gr = n0 + (r - BM);
+      sp[c] = wsc + (gr < n ? gr : n - 1) * nblk;
+    }
   }
+  // swizzle keys of this lane's operand rows (the same for all its rows)
+  const int akey = Swz<XR>::key(l32), bkey = Swz<WR>::key(l32);
+  const int ach0 = ((ABITS == 4 ? 2 * h : h) ^ akey) << 4, ach1 = ((ABITS == 4 ? 2 * h + 1 : h + 2) ^ akey) << 4;
+  const int ahi0 = ((4 + h) ^ akey) << 4, ahi1 = ((6 + h) ^ akey) << 4;
+  const int bch0 = ((BBITS == 4 ? 2 * h : h) ^ bkey) << 4, bch1 = ((BBITS == 4 ? 2 * h + 1 : h + 2) ^ bkey) << 4;
+  const int bhi0 = ((4 + h) ^ bkey) << 4, bhi1 = ((6 + h) ^ bkey) << 4;
+  const int arow = (wm * WTM + l32) * XR, brow = (wn * WTN + l32) * WR;
+  const int asrow = (wm * WTM + l32) * TRIP, bsrow = (BM + wn * WTN + l32) * TRIP;
 
   f32x16_t acc[MT][NT];
 #pragma unroll
@@ -113,67 +157,68 @@ mxmma_kernel(const uint8_t *__restrict__ xc, const uint8_t *__restrict__ xsc, co
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  const int KT = (int)(k / BKX);
   struct Slot {
-    u32x4_t x[XCH];
-    WSlot<FB> w[NT];
-    uint32_t xs2[MT];  // X scale byte pairs of this lane's rows
+    u32x4_t x[XCH], w[WCH];
   };
   Slot G[D];
+  uint32_t R[SCH];  // scale dwords of the next trip
 
   auto load = [&](Slot &g, int kt) __attribute__((always_inline)) {
-    const int64_t k0 = (int64_t)kt * BKX;
 #pragma unroll
-    for (int c = 0; c < XCH; ++c) g.x[c] = *reinterpret_cast<const u32x4_t *>(xp[c] + k0 * ABITS / 8);
+    for (int c = 0; c < XCH; ++c) g.x[c] = *reinterpret_cast<const u32x4_t *>(xp[c] + (int64_t)kt * XR);
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-#pragma unroll
-      for (int q = 0; q < BBITS / 2; ++q)
-        g.w[j].c[q] = *reinterpret_cast<const u32x4_t *>(wp[j] + k0 * BBITS / 8 + (BBITS == 4 ? 16 : 32) * q);
-      g.w[j].s = *reinterpret_cast<const uint16_t *>(wsp[j] + k0 / 32);
-    }
-#pragma unroll
-    for (int i = 0; i < MT; ++i) g.xs2[i] = *reinterpret_cast<const uint16_t *>(xsp[i] + k0 / 32);
+    for (int c = 0; c < WCH; ++c) g.w[c] = *reinterpret_cast<const u32x4_t *>(wp[c] + (int64_t)kt * WR);
   };
-  auto store_x = [&](const Slot &g, int buf) __attribute__((always_inline)) {
+  auto store = [&](const Slot &g, int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int c = 0; c < XCH; ++c) {
-      const int cid = c * NTHR + tid;
-      *reinterpret_cast<u32x4_t *>(&xs[buf][(cid / CPR) * LDX + (cid % CPR) * 16]) = g.x[c];
-    }
+    for (int c = 0; c < XCH; ++c) *reinterpret_cast<u32x4_t *>(&xs[buf][xd + c * XRS * XR]) = g.x[c];
+#pragma unroll
+    for (int c = 0; c < WCH; ++c) *reinterpret_cast<u32x4_t *>(&ws[buf][wd + c * WRS * WR]) = g.w[c];
   };
-  auto step = [&](auto guard, int kt, Slot &cur, const Slot &nxt) __attribute__((always_inline)) {
+  // scales of trip tr; steps past the end are clamped to the last one, so a
+  // partial (or nonexistent) trip reads in bounds
+  auto load_sc = [&](int tr) __attribute__((always_inline)) {
+    const int st = min(tr * TRIP + sst, KT - 1);
+#pragma unroll
+    for (int c = 0; c < SCH; ++c) R[c] = *reinterpret_cast<const uint32_t *>(sp[c] + 4 * st);
+  };
+  auto store_sc = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < SCH; ++c) ss[buf][c * NTHR + tid] = R[c];
+  };
+
+  // one step: kt the step, S = kt % TRIP
+  auto step = [&](auto guard, int kt, int S, Slot &cur, const Slot &nxt) __attribute__((always_inline)) {
     constexpr bool kGuard = decltype(guard)::value;
-    const uint8_t *xb = xs[kt & 1];
-    // A operands of both slices: 16 (4-bit) or 2 x 16 (8-bit) bytes per lane each
-    i32x8_t a[2][MT];
+    const uint8_t *xb = xs[kt & 1] + arow;
+    const uint8_t *wb = ws[kt & 1] + brow;
+    const uint32_t *sb = ss[(kt / TRIP) & 1];
+    i32x8_t a[2][MT], b[2][NT];
+    uint32_t as[MT], bs[NT];
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int s = 0; s < 2; ++s) {
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
-        const uint8_t *row = &xb[(wm * WTM + i * 32 + l32) * LDX];
-        const u32x4_t lo = *reinterpret_cast<const u32x4_t *>(row + (ABITS == 4 ? 32 * h + 16 * s : 16 * h + 32 * s));
-        const u32x4_t hi = ABITS == 8 ? *reinterpret_cast<const u32x4_t *>(row + 64 + 16 * h + 32 * s) : u32x4_t{0, 0, 0, 0};
+        const uint8_t *row = xb + i * 32 * XR;
+        const u32x4_t lo = *reinterpret_cast<const u32x4_t *>(row + (s ? ach1 : ach0));
+        const u32x4_t hi = ABITS == 8 ? *reinterpret_cast<const u32x4_t *>(row + (s ? ahi1 : ahi0))
+                                      : u32x4_t{0, 0, 0, 0};
         a[s][i] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
-    i32x8_t b[2][NT];
-    uint32_t bs[NT], as[MT];
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      bs[j] = cur.w[j].s;
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        if constexpr (BBITS == 4) {
-          const u32x4_t c = cur.w[j].c[s];
-          b[s][j] = i32x8_t{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
-        } else {
-          const u32x4_t c0 = cur.w[j].c[s], c1 = cur.w[j].c[2 + s];
-          b[s][j] = i32x8_t{(int)c0.x, (int)c0.y, (int)c0.z, (int)c0.w, (int)c1.x, (int)c1.y, (int)c1.z, (int)c1.w};
-        }
+      for (int j = 0; j < NT; ++j) {
+        const uint8_t *row = wb + j * 32 * WR;
+        const u32x4_t lo = *reinterpret_cast<const u32x4_t *>(row + (s ? bch1 : bch0));
+        const u32x4_t hi = BBITS == 8 ? *reinterpret_cast<const u32x4_t *>(row + (s ? bhi1 : bhi0))
+                                      : u32x4_t{0, 0, 0, 0};
+        b[s][j] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
     }
+    // scale bytes of blocks 4kt+2h and 4kt+2h+1, in bytes 0 and 1
 #pragma unroll
-    for (int i = 0; i < MT; ++i) as[i] = cur.xs2[i];
+    for (int i = 0; i < MT; ++i) as[i] = sb[asrow + i * 32 * TRIP + S] >> (16 * h);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) bs[j] = sb[bsrow + j * 32 * TRIP + S] >> (16 * h);
     __builtin_amdgcn_sched_barrier(0);
     if (!kGuard || kt + D < KT) load(cur, kt + D);
 #pragma unroll
@@ -190,26 +235,36 @@ mxmma_kernel(const uint8_t *__restrict__ xc, const uint8_t *__restrict__ xsc, co
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[1][i], b[1][j], acc[i][j], MxFmt<FA>::kCode,
                                                                        MxFmt<FB>::kCode, 1, (int)as[i], 1, (int)bs[j]);
         }
-    if (!kGuard || kt + 1 < KT) store_x(nxt, (kt + 1) & 1);
+    if (!kGuard || kt + 1 < KT) store(nxt, (kt + 1) & 1);
+    if (S == TRIP - 1 && (!kGuard || kt + 1 < KT)) {
+      // trip boundary: publish the next trip's scales, fetch the one after
+      store_sc(((kt / TRIP) + 1) & 1);
+      load_sc(kt / TRIP + 2);
+    }
     __syncthreads();
   };
   constexpr std::integral_constant<bool, false> kFast{};
   constexpr std::integral_constant<bool, true> kGuarded{};
 
+  load_sc(0);
 #pragma unroll
   for (int s = 0; s < D; ++s)
     if (s < KT) load(G[s], s);
-  store_x(G[0], 0);
+  store_sc(0);
+  load_sc(1);
+  store(G[0], 0);
   __syncthreads();
   int kt = 0;
-  for (; kt + UK + D <= KT; kt += UK) {
+  // steady state: whole trips whose code prefetches all stay in range
+  for (; kt + TRIP + D <= KT; kt += TRIP) {
 #pragma unroll
-    for (int S = 0; S < UK; ++S) step(kFast, kt + S, G[S % D], G[(S + 1) % D]);
+    for (int S = 0; S < TRIP; ++S) step(kFast, kt + S, S, G[S % D], G[(S + 1) % D]);
   }
+  // guarded drain (kt is a multiple of TRIP, hence of D, here)
   for (; kt < KT; kt += D) {
 #pragma unroll
     for (int S = 0; S < D; ++S)
-      if (kt + S < KT) step(kGuarded, kt + S, G[S], G[(S + 1) % D]);
+      if (kt + S < KT) step(kGuarded, kt + S, (kt + S) % TRIP, G[S], G[(S + 1) % D]);
   }
 
 #pragma unroll
@@ -230,13 +285,13 @@ mxmma_kernel(const uint8_t *__restrict__ xc, const uint8_t *__restrict__ xsc, co
   }
 }
 
-template <int FA, int FB, int BM, int BN>
+template <int FA, int FB, int BM, int BN, int D, int GM>
 hipError_t run_cfg(const void *xc, const void *xs, const void *wc, const void *ws, int64_t m, int64_t n, int64_t k,
                    void *out, int ot, hipStream_t s) {
   const int tiles_m = (int)((m + BM - 1) / BM), tiles_n = (int)((n + BN - 1) / BN);
-  hipLaunchKernelGGL((mxmma_kernel<FA, FB, BM, BN, 2, 2, 2, 4>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, s,
-                     (const uint8_t *)xc, (const uint8_t *)xs, (const uint8_t *)wc, (const uint8_t *)ws, out, ot, m, n,
-                     k, tiles_m, tiles_n);
+  hipLaunchKernelGGL((mxmma_kernel<FA, FB, BM, BN, 2, 2, D, GM>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0,
+                     s, (const uint8_t *)xc, (const uint8_t *)xs, (const uint8_t *)wc, (const uint8_t *)ws, out, ot, m,
+                     n, k, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
@@ -245,8 +300,8 @@ hipError_t run_ab(const void *xc, const void *xs, const void *wc, const void *ws
                   void *out, int ot, hipStream_t s) {
   if ((m + 127) / 128 * ((n + 63) / 64) > (int64_t)1 << 30) return hipErrorInvalidValue;
   const int64_t big = ((m + 255) / 256) * ((n + 127) / 128);
-  if (big >= 256) return run_cfg<FA, FB, 256, 128>(xc, xs, wc, ws, m, n, k, out, ot, s);
-  return run_cfg<FA, FB, 128, 64>(xc, xs, wc, ws, m, n, k, out, ot, s);
+  if (big >= 256) return run_cfg<FA, FB, 256, 128, 2, 4>(xc, xs, wc, ws, m, n, k, out, ot, s);
+  return run_cfg<FA, FB, 128, 64, 2, 4>(xc, xs, wc, ws, m, n, k, out, ot, s);
 }
 
 template <int FA>

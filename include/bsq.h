@@ -125,7 +125,7 @@ bsq_status bsq_quantize(bsq_format fmt, int block, const void *w, bsq_dtype wt, 
  * sum dec(a) * dec(b) in fp32 [rlx-cpu quant.rs, lowp_scaled_matmul].  This is
  * an activation-quantized contract: X is first packed with bsq_quantize.
  * k must be a multiple of 128 (BSQ_ERR_SHAPE otherwise); codes 16-byte
- * aligned, scales 2-byte aligned.  out: device [m,n], f32 or bf16 (RNE). */
+ * aligned, scales 4-byte aligned.  out: device [m,n], f32 or bf16 (RNE). */
 bsq_status bsq_qgemm_mx(bsq_format xfmt, const void *x_codes, const void *x_scales, bsq_format wfmt,
                         const void *w_codes, const void *w_scales, int64_t m, int64_t n, int64_t k, void *out,
                         bsq_dtype ot, void *stream);
