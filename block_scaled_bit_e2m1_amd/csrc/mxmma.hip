@@ -58,8 +58,9 @@ template <> struct MxFmt<kMXFP4> { static constexpr int kCode = 4, kBits = 4; };
 
 // LDS tile with RB-byte rows: byte offset of 16-byte chunk c of row r.  The
 // chunk index is XORed with a key of the row so that 16 consecutive rows at
-// one chunk, and the chunks of consecutive rows, fall on distinct banks
-// (64 banks x 4 bytes = 256 bytes per pass).
+// one chunk, and the chunks of consecutive rows, fall on distinct banks (a
+// 16-byte LDS access serves 16 lanes per pass over 64 banks x 4 bytes; the
+// bank-conflict counter confirms this model against a 32-bank one).
 template <int RB> struct Swz {
   static constexpr int kCPR = RB / 16, kRPB = 256 / RB;
   static constexpr int kPeriod = kCPR * kRPB;  // rows after which the key repeats
@@ -89,9 +90,20 @@ mxmma_kernel(const uint8_t *__restrict__ xc, const uint8_t *__restrict__ xsc, co
                     32 % Swz<WR>::kPeriod == 0,
                 "one swizzle key per lane");
   static_assert(TRIP % D == 0, "the prefetch ring must divide a trip");
-  __shared__ __attribute__((aligned(16))) uint8_t xs[2][BM * XR];
-  __shared__ __attribute__((aligned(16))) uint8_t ws[2][BN * WR];
-  __shared__ uint32_t ss[2][(BM + BN) * TRIP];
+  // three code buffers: step kt is read while step kt+1 is complete (so its
+  // first fragments can be fetched early) and step kt+2 is being written
+  constexpr int NB = 3;
+  // scales as [step of the trip][row], the step stride padded to 16 mod 64
+  // words so that the writes (4 steps x 16 rows per pass) and the per-step
+  // column reads both spread over all banks
+  constexpr int SS = BM + BN + 16;
+  constexpr int XB = BM * XR, WB = BN * WR;  // bytes of one code buffer
+  // one LDS array: X buffers, W buffers, scale buffers (the epilogue reuses
+  // the code buffers for staging)
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NB * (XB + WB) + 2 * TRIP * SS * 4];
+  auto xs = [&](int b) __attribute__((always_inline)) { return smem + b * XB; };
+  auto ws = [&](int b) __attribute__((always_inline)) { return smem + NB * XB + b * WB; };
+  uint32_t(*ss)[TRIP * SS] = reinterpret_cast<uint32_t(*)[TRIP * SS]>(smem + NB * (XB + WB));
 
   // tile order: XCD x runs tiles [x*T/8, (x+1)*T/8) (blocks are dealt to the
   // XCDs round-robin), walked as GM m-tiles by consecutive n-tiles
@@ -147,7 +159,8 @@ mxmma_kernel(const uint8_t *__restrict__ xc, const uint8_t *__restrict__ xsc, co
   const int bch0 = ((BBITS == 4 ? 2 * h : h) ^ bkey) << 4, bch1 = ((BBITS == 4 ? 2 * h + 1 : h + 2) ^ bkey) << 4;
   const int bhi0 = ((4 + h) ^ bkey) << 4, bhi1 = ((6 + h) ^ bkey) << 4;
   const int arow = (wm * WTM + l32) * XR, brow = (wn * WTN + l32) * WR;
-  const int asrow = (wm * WTM + l32) * TRIP, bsrow = (BM + wn * WTN + l32) * TRIP;
+  const int asrow = wm * WTM + l32, bsrow = BM + wn * WTN + l32;
+  const int sw = (tid / TRIP) + sst * SS;  // this thread's scale item 0 in the LDS layout
 
   f32x16_t acc[MT][NT];
 #pragma unroll
@@ -171,9 +184,9 @@ mxmma_kernel(const uint8_t *__restrict__ xc, const uint8_t *__restrict__ xsc, co
   };
   auto store = [&](const Slot &g, int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int c = 0; c < XCH; ++c) *reinterpret_cast<u32x4_t *>(&xs[buf][xd + c * XRS * XR]) = g.x[c];
+    for (int c = 0; c < XCH; ++c) *reinterpret_cast<u32x4_t *>(&xs(buf)[xd + c * XRS * XR]) = g.x[c];
 #pragma unroll
-    for (int c = 0; c < WCH; ++c) *reinterpret_cast<u32x4_t *>(&ws[buf][wd + c * WRS * WR]) = g.w[c];
+    for (int c = 0; c < WCH; ++c) *reinterpret_cast<u32x4_t *>(&ws(buf)[wd + c * WRS * WR]) = g.w[c];
   };
   // scales of trip tr; steps past the end are clamped to the last one, so a
   // partial (or nonexistent) trip reads in bounds
@@ -184,112 +197,186 @@ mxmma_kernel(const uint8_t *__restrict__ xc, const uint8_t *__restrict__ xsc, co
   };
   auto store_sc = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int c = 0; c < SCH; ++c) ss[buf][c * NTHR + tid] = R[c];
+    for (int c = 0; c < SCH; ++c) ss[buf][sw + c * (NTHR / TRIP)] = R[c];
   };
 
-  // one step: kt the step, S = kt % TRIP
-  auto step = [&](auto guard, int kt, int S, Slot &cur, const Slot &nxt) __attribute__((always_inline)) {
-    constexpr bool kGuard = decltype(guard)::value;
-    const uint8_t *xb = xs[kt & 1] + arow;
-    const uint8_t *wb = ws[kt & 1] + brow;
-    const uint32_t *sb = ss[(kt / TRIP) & 1];
-    i32x8_t a[2][MT], b[2][NT];
-    uint32_t as[MT], bs[NT];
+  // operand fragments of slice s from the LDS tiles of buffer buf
+  auto read = [&](int buf, int s, i32x8_t a[MT], i32x8_t b[NT]) __attribute__((always_inline)) {
+    const uint8_t *xb = xs(buf) + arow;
+    const uint8_t *wb = ws(buf) + brow;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-#pragma unroll
-      for (int i = 0; i < MT; ++i) {
-        const uint8_t *row = xb + i * 32 * XR;
-        const u32x4_t lo = *reinterpret_cast<const u32x4_t *>(row + (s ? ach1 : ach0));
-        const u32x4_t hi = ABITS == 8 ? *reinterpret_cast<const u32x4_t *>(row + (s ? ahi1 : ahi0))
-                                      : u32x4_t{0, 0, 0, 0};
-        a[s][i] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      }
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const uint8_t *row = wb + j * 32 * WR;
-        const u32x4_t lo = *reinterpret_cast<const u32x4_t *>(row + (s ? bch1 : bch0));
-        const u32x4_t hi = BBITS == 8 ? *reinterpret_cast<const u32x4_t *>(row + (s ? bhi1 : bhi0))
-                                      : u32x4_t{0, 0, 0, 0};
-        b[s][j] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      }
+    for (int i = 0; i < MT; ++i) {
+      const uint8_t *row = xb + i * 32 * XR;
+      const u32x4_t lo = *reinterpret_cast<const u32x4_t *>(row + (s ? ach1 : ach0));
+      const u32x4_t hi =
+          ABITS == 8 ? *reinterpret_cast<const u32x4_t *>(row + (s ? ahi1 : ahi0)) : u32x4_t{0, 0, 0, 0};
+      a[i] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
-    // scale bytes of blocks 4kt+2h and 4kt+2h+1, in bytes 0 and 1
 #pragma unroll
-    for (int i = 0; i < MT; ++i) as[i] = sb[asrow + i * 32 * TRIP + S] >> (16 * h);
+    for (int j = 0; j < NT; ++j) {
+      const uint8_t *row = wb + j * 32 * WR;
+      const u32x4_t lo = *reinterpret_cast<const u32x4_t *>(row + (s ? bch1 : bch0));
+      const u32x4_t hi =
+          BBITS == 8 ? *reinterpret_cast<const u32x4_t *>(row + (s ? bhi1 : bhi0)) : u32x4_t{0, 0, 0, 0};
+      b[j] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+  };
+  // the 2x MT x NT MFMAs of slice s; the scale operand's byte s is this lane's E8M0 for slice s
+  auto mma = [&](auto sl, const i32x8_t a[MT], const i32x8_t b[NT], const uint32_t as[MT], const uint32_t bs[NT])
+                 __attribute__((always_inline)) {
+    constexpr int s = decltype(sl)::value;
 #pragma unroll
-    for (int j = 0; j < NT; ++j) bs[j] = sb[bsrow + j * 32 * TRIP + S] >> (16 * h);
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], MxFmt<FA>::kCode,
+                                                                   MxFmt<FB>::kCode, s, (int)as[i], s, (int)bs[j]);
+  };
+  constexpr std::integral_constant<int, 0> kS0{};
+  constexpr std::integral_constant<int, 1> kS1{};
+  // scale bytes of step kt for this lane's rows: blocks 4kt+2h and 4kt+2h+1 in bytes 0 and 1
+  auto read_sc = [&](int kt, uint32_t as[MT], uint32_t bs[NT]) __attribute__((always_inline)) {
+    const uint32_t *sb = ss[(kt / TRIP) & 1] + (kt % TRIP) * SS;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) as[i] = sb[asrow + i * 32] >> (16 * h);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) bs[j] = sb[bsrow + j * 32] >> (16 * h);
+  };
+
+  // loop-carried: slice-0 fragments and scale bytes of the current step
+  i32x8_t a0[MT], b0[NT];
+  uint32_t as[MT], bs[NT];
+
+  // One step kt (S = kt % TRIP).  Code buffer kt%NB holds step kt and
+  // (kt+1)%NB step kt+1 (complete since the last barrier); the register
+  // slots hold steps kt+2 .. kt+1+D, step q in slot q%D.  The step writes
+  // step kt+2 from its slot sl into buffer (kt+2)%NB, which nobody reads
+  // until after the barrier, then refills sl with the loads of step kt+2+D.
+  auto step = [&](auto guard, int kt, int S, Slot &sl) __attribute__((always_inline)) {
+    constexpr bool kGuard = decltype(guard)::value;
+    const bool more = !kGuard || kt + 1 < KT;
+    i32x8_t a1[MT], b1[NT];
+    uint32_t asn[MT], bsn[NT];
+    // phase 1: slice-1 fragments go out, then the slice-0 MFMAs on operands
+    // fetched during the previous step
+    read(kt % NB, 1, a1, b1);
+    mma(kS0, a0, b0, as, bs);
     __builtin_amdgcn_sched_barrier(0);
-    if (!kGuard || kt + D < KT) load(cur, kt + D);
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          // the scale operand's byte s is this lane's E8M0 for slice s
-          if (s == 0)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[0][i], b[0][j], acc[i][j], MxFmt<FA>::kCode,
-                                                                       MxFmt<FB>::kCode, 0, (int)as[i], 0, (int)bs[j]);
-          else
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[1][i], b[1][j], acc[i][j], MxFmt<FA>::kCode,
-                                                                       MxFmt<FB>::kCode, 1, (int)as[i], 1, (int)bs[j]);
-        }
-    if (!kGuard || kt + 1 < KT) store(nxt, (kt + 1) & 1);
-    if (S == TRIP - 1 && (!kGuard || kt + 1 < KT)) {
-      // trip boundary: publish the next trip's scales, fetch the one after
+    // phase 2: the next step's slice-0 fragments and scales, the slice-1
+    // MFMAs, then the LDS writes of step kt+2 (their loads have had D steps)
+    // and the global loads of step kt+2+D
+    if (more) {
+      read((kt + 1) % NB, 0, a0, b0);
+      read_sc(kt + 1, asn, bsn);
+    }
+    mma(kS1, a1, b1, as, bs);
+    if (!kGuard || kt + 2 < KT) store(sl, (kt + 2) % NB);
+    if (!kGuard || kt + 2 + D < KT) load(sl, kt + 2 + D);
+    if (S == TRIP - 2 && more) {
+      // publish the next trip's scales one step early (the last step of this
+      // trip reads them ahead), fetch the trip after
       store_sc(((kt / TRIP) + 1) & 1);
       load_sc(kt / TRIP + 2);
     }
+#pragma unroll
+    for (int i = 0; i < MT; ++i) as[i] = asn[i];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) bs[j] = bsn[j];
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
   };
   constexpr std::integral_constant<bool, false> kFast{};
   constexpr std::integral_constant<bool, true> kGuarded{};
 
+  // prologue: trip-0 scales and steps 0 and 1 into LDS, steps 2..D+1 in flight
   load_sc(0);
-#pragma unroll
-  for (int s = 0; s < D; ++s)
-    if (s < KT) load(G[s], s);
+  load(G[0], 0);
   store_sc(0);
   load_sc(1);
   store(G[0], 0);
-  __syncthreads();
-  int kt = 0;
-  // steady state: whole trips whose code prefetches all stay in range
-  for (; kt + TRIP + D <= KT; kt += TRIP) {
+  if (KT > 1) {
+    load(G[0], 1);
+    store(G[0], 1);
+  }
 #pragma unroll
-    for (int S = 0; S < TRIP; ++S) step(kFast, kt + S, S, G[S % D], G[(S + 1) % D]);
+  for (int q = 2; q < 2 + D; ++q)
+    if (q < KT) load(G[q % D], q);
+  __syncthreads();
+  read(0, 0, a0, b0);
+  read_sc(0, as, bs);
+  int kt = 0;
+  // steady state: whole trips whose loads, writes and reads all stay in range
+  for (; kt + TRIP + D + 2 <= KT; kt += TRIP) {
+#pragma unroll
+    for (int S = 0; S < TRIP; ++S) step(kFast, kt + S, S, G[(S + 2) % D]);
   }
   // guarded drain (kt is a multiple of TRIP, hence of D, here)
   for (; kt < KT; kt += D) {
 #pragma unroll
     for (int S = 0; S < D; ++S)
-      if (kt + S < KT) step(kGuarded, kt + S, (kt + S) % TRIP, G[S], G[(S + 1) % D]);
+      if (kt + S < KT) step(kGuarded, kt + S, (kt + S) % TRIP, G[(S + 2) % D]);
   }
 
+  // Epilogue.  An accumulator lane holds 4-row runs of one column, so direct
+  // stores would write 2- or 4-byte pieces.  Instead each 32-row band of the
+  // wave tile is staged in LDS (the code buffers are free now) and read back
+  // as 16-byte row pieces, so one store instruction writes whole row runs.
+  __syncthreads();
+  auto epilogue = [&](auto es_tag) __attribute__((always_inline)) {
+    constexpr int ES = decltype(es_tag)::value;  // output element bytes
+    constexpr int EV = 16 / ES;                  // elements per 16-byte piece
+    constexpr int RS = WTN * ES + 16;            // staged row stride (padded against bank conflicts)
+    constexpr int LPR = WTN * ES / 16;           // lanes per staged row
+    constexpr int RPI = 64 / LPR;                // rows per read-back instruction
+    static_assert(WGM * WGN * 32 * RS <= NB * (XB + WB), "staging must fit in the code buffers");
+    uint8_t *st = smem + wid * 32 * RS;
+    const bool vec = n % EV == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
+    const int lr = lane / LPR, lc = (lane % LPR) * EV;
+    const int64_t gc = n0 + wn * WTN + lc;
 #pragma unroll
-  for (int i = 0; i < MT; ++i) {
+    for (int i = 0; i < MT; ++i) {
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const int64_t col = n0 + wn * WTN + j * 32 + l32;
-      if (col >= n) continue;
+      for (int j = 0; j < NT; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = m0 + wm * WTM + i * 32 + (v >> 2) * 8 + h * 4 + (v & 3);
-        if (row >= m) continue;
-        const float val = acc[i][j][v];
-        if (ot == 0) reinterpret_cast<float *>(out)[row * n + col] = val;
-        else reinterpret_cast<uint16_t *>(out)[row * n + col] = f32_to_bf16_bits(val);
+        for (int v = 0; v < 16; ++v) {
+          const int r = (v >> 2) * 8 + h * 4 + (v & 3), c = j * 32 + l32;
+          if constexpr (ES == 4) *reinterpret_cast<float *>(st + r * RS + c * 4) = acc[i][j][v];
+          else *reinterpret_cast<uint16_t *>(st + r * RS + c * 2) = f32_to_bf16_bits(acc[i][j][v]);
+        }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < 32 / RPI; ++q) {
+        const int r = q * RPI + lr;
+        const u32x4_t val = *reinterpret_cast<const u32x4_t *>(st + r * RS + lc * ES);
+        const int64_t gr = m0 + wm * WTM + i * 32 + r;
+        if (gr >= m) continue;
+        uint8_t *dst = reinterpret_cast<uint8_t *>(out) + (gr * n + gc) * ES;
+        if (vec && gc + EV <= n) {
+          *reinterpret_cast<u32x4_t *>(dst) = val;
+        } else {
+#pragma unroll
+          for (int e = 0; e < EV; ++e) {
+            const uint32_t word = val[e * ES / 4];
+            if (gc + e < n) {
+              if constexpr (ES == 4) reinterpret_cast<uint32_t *>(dst)[e] = word;
+              else reinterpret_cast<uint16_t *>(dst)[e] = (uint16_t)(word >> (16 * (e & 1)));
+            }
+          }
+        }
       }
+      __syncthreads();
     }
-  }
+  };
+  if (ot == 0) epilogue(std::integral_constant<int, 4>{});
+  else epilogue(std::integral_constant<int, 2>{});
 }
 
-template <int FA, int FB, int BM, int BN, int D, int GM>
+template <int FA, int FB, int BM, int BN, int D, int GM, int WGM = 2, int WGN = 2>
 hipError_t run_cfg(const void *xc, const void *xs, const void *wc, const void *ws, int64_t m, int64_t n, int64_t k,
                    void *out, int ot, hipStream_t s) {
   const int tiles_m = (int)((m + BM - 1) / BM), tiles_n = (int)((n + BN - 1) / BN);
-  hipLaunchKernelGGL((mxmma_kernel<FA, FB, BM, BN, 2, 2, D, GM>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0,
+  hipLaunchKernelGGL((mxmma_kernel<FA, FB, BM, BN, WGM, WGN, D, GM>), dim3((unsigned)(tiles_m * tiles_n)),
+                     dim3(WGM * WGN * 64), 0,
                      s, (const uint8_t *)xc, (const uint8_t *)xs, (const uint8_t *)wc, (const uint8_t *)ws, out, ot, m,
                      n, k, tiles_m, tiles_n);
   return hipGetLastError();
@@ -300,8 +387,17 @@ hipError_t run_ab(const void *xc, const void *xs, const void *wc, const void *ws
                   void *out, int ot, hipStream_t s) {
   if ((m + 127) / 128 * ((n + 63) / 64) > (int64_t)1 << 30) return hipErrorInvalidValue;
   const int64_t big = ((m + 255) / 256) * ((n + 127) / 128);
-  if (big >= 256) return run_cfg<FA, FB, 256, 128, 2, 4>(xc, xs, wc, ws, m, n, k, out, ot, s);
-  return run_cfg<FA, FB, 128, 64, 2, 4>(xc, xs, wc, ws, m, n, k, out, ot, s);
+  // Measured on 2048x4096x4096: one-step register prefetch everywhere; two
+  // waves per SIMD (8-wave workgroups) where the registers allow it (4-bit
+  // operands on both sides, or one 8-bit side), one wave per SIMD with both
+  // operands 8-bit (8 waves would spill).
+  constexpr int A8 = MxFmt<FA>::kBits == 8, B8 = MxFmt<FB>::kBits == 8;
+  if (big >= 256) {
+    if constexpr (A8 && B8) return run_cfg<FA, FB, 256, 128, 1, 4, 2, 2>(xc, xs, wc, ws, m, n, k, out, ot, s);
+    else if constexpr (A8 || B8) return run_cfg<FA, FB, 256, 128, 1, 4, 4, 2>(xc, xs, wc, ws, m, n, k, out, ot, s);
+    else return run_cfg<FA, FB, 256, 128, 1, 4, 2, 4>(xc, xs, wc, ws, m, n, k, out, ot, s);
+  }
+  return run_cfg<FA, FB, 128, 64, 1, 4, 2, 2>(xc, xs, wc, ws, m, n, k, out, ot, s);
 }
 
 template <int FA>
