@@ -36,6 +36,7 @@
 //    each XCD a contiguous run of tiles that share X rows (one L2 per XCD).
 #include "bsq_internal.hpp"
 #include "codec.hpp"
+#include "epilogue.hpp"
 
 #include <type_traits>
 
@@ -407,23 +408,13 @@ mfma_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
   }
 
   // ---- epilogue ----
-#pragma unroll
-  for (int i = 0; i < MT; ++i) {
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const int64_t col = n0 + wn * WTN + j * 32 + l32;
-      if (col >= n) continue;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = m0 + wm * WTM + i * 32 + (v >> 2) * 8 + h * 4 + (v & 3);
-        if (row >= m) continue;
-        float val = acc[i][j][v];
-        if constexpr (F == kNVFP4) val *= global;
-        if (ot == 0) reinterpret_cast<float *>(out)[row * n + col] = val;
-        else reinterpret_cast<uint16_t *>(out)[row * n + col] = f32_to_bf16_bits(val);
-      }
-    }
-  }
+  // epilogue: the X buffers are free now; each wave stages its tile there
+  // (the nvfp4 global is applied here, once per output)
+  static_assert(epi::stage_bytes<WTN, WGM * WGN>() <= 2 * BM * LDS_LD * 2, "staging must fit in the X buffers");
+  __syncthreads();
+  epi::store_acc<MT, NT, WTN>(acc, F == kNVFP4 ? global : 1.0f,
+                              reinterpret_cast<uint8_t *>(&xs[0][0]) + wid * 32 * epi::row_stride<WTN, 4>(), lane,
+                              m0 + wm * WTM, n0 + wn * WTN, m, n, out, ot);
 }
 
 template <int F, int BM, int BN, int WGM, int WGN, int D, int UK, bool ROT = false, int SCHED = 1>

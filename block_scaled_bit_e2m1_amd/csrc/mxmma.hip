@@ -35,6 +35,7 @@
 // bounds the W and X bytes one L2 must hold.
 #include "bsq_internal.hpp"
 #include "codec.hpp"
+#include "epilogue.hpp"
 
 #include <type_traits>
 
@@ -317,58 +318,11 @@ mxmma_kernel(const uint8_t *__restrict__ xc, const uint8_t *__restrict__ xsc, co
       if (kt + S < KT) step(kGuarded, kt + S, (kt + S) % TRIP, G[(S + 2) % D]);
   }
 
-  // Epilogue.  An accumulator lane holds 4-row runs of one column, so direct
-  // stores would write 2- or 4-byte pieces.  Instead each 32-row band of the
-  // wave tile is staged in LDS (the code buffers are free now) and read back
-  // as 16-byte row pieces, so one store instruction writes whole row runs.
+  // epilogue: the code buffers are free now; each wave stages its tile there
+  static_assert(epi::stage_bytes<WTN, WGM * WGN>() <= NB * (XB + WB), "staging must fit in the code buffers");
   __syncthreads();
-  auto epilogue = [&](auto es_tag) __attribute__((always_inline)) {
-    constexpr int ES = decltype(es_tag)::value;  // output element bytes
-    constexpr int EV = 16 / ES;                  // elements per 16-byte piece
-    constexpr int RS = WTN * ES + 16;            // staged row stride (padded against bank conflicts)
-    constexpr int LPR = WTN * ES / 16;           // lanes per staged row
-    constexpr int RPI = 64 / LPR;                // rows per read-back instruction
-    static_assert(WGM * WGN * 32 * RS <= NB * (XB + WB), "staging must fit in the code buffers");
-    uint8_t *st = smem + wid * 32 * RS;
-    const bool vec = n % EV == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
-    const int lr = lane / LPR, lc = (lane % LPR) * EV;
-    const int64_t gc = n0 + wn * WTN + lc;
-#pragma unroll
-    for (int i = 0; i < MT; ++i) {
-#pragma unroll
-      for (int j = 0; j < NT; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = (v >> 2) * 8 + h * 4 + (v & 3), c = j * 32 + l32;
-          if constexpr (ES == 4) *reinterpret_cast<float *>(st + r * RS + c * 4) = acc[i][j][v];
-          else *reinterpret_cast<uint16_t *>(st + r * RS + c * 2) = f32_to_bf16_bits(acc[i][j][v]);
-        }
-      __syncthreads();
-#pragma unroll
-      for (int q = 0; q < 32 / RPI; ++q) {
-        const int r = q * RPI + lr;
-        const u32x4_t val = *reinterpret_cast<const u32x4_t *>(st + r * RS + lc * ES);
-        const int64_t gr = m0 + wm * WTM + i * 32 + r;
-        if (gr >= m) continue;
-        uint8_t *dst = reinterpret_cast<uint8_t *>(out) + (gr * n + gc) * ES;
-        if (vec && gc + EV <= n) {
-          *reinterpret_cast<u32x4_t *>(dst) = val;
-        } else {
-#pragma unroll
-          for (int e = 0; e < EV; ++e) {
-            const uint32_t word = val[e * ES / 4];
-            if (gc + e < n) {
-              if constexpr (ES == 4) reinterpret_cast<uint32_t *>(dst)[e] = word;
-              else reinterpret_cast<uint16_t *>(dst)[e] = (uint16_t)(word >> (16 * (e & 1)));
-            }
-          }
-        }
-      }
-      __syncthreads();
-    }
-  };
-  if (ot == 0) epilogue(std::integral_constant<int, 4>{});
-  else epilogue(std::integral_constant<int, 2>{});
+  epi::store_acc<MT, NT, WTN>(acc, 1.0f, smem + wid * 32 * epi::row_stride<WTN, 4>(), lane, m0 + wm * WTM,
+                              n0 + wn * WTN, m, n, out, ot);
 }
 
 template <int FA, int FB, int BM, int BN, int D, int GM, int WGM = 2, int WGN = 2>
