@@ -36,8 +36,14 @@ MFMA_FP8_PEAK_TFLOPS = 5000.0   # dense fp8 (an fp8 operand on either side of th
 MFMA_FP4_PEAK_TFLOPS = 10100.0  # dense fp4 (both operands fp4)
 ROTATE_BYTES = 640 << 20        # distinct weight copies per rotation (> 2x the 256 MB MALL)
 
-KERNEL_SOURCES = {"qgemv": "block_scaled_bit_e2m1_amd/csrc/rows.hip",
-                  "qgemm": "block_scaled_bit_e2m1_amd/csrc/mfma.hip"}
+# sources each timed kernel is compiled from: traffic counters taken on an
+# older version of any of them are not reported
+KERNEL_SOURCES = {"qgemv": ["block_scaled_bit_e2m1_amd/csrc/rows.hip", "block_scaled_bit_e2m1_amd/csrc/codec.hpp"],
+                  "qgemm": ["block_scaled_bit_e2m1_amd/csrc/mfma.hip", "block_scaled_bit_e2m1_amd/csrc/codec.hpp",
+                            "block_scaled_bit_e2m1_amd/csrc/epilogue.hpp"],
+                  "qgemm_mx": ["block_scaled_bit_e2m1_amd/csrc/mxmma.hip", "block_scaled_bit_e2m1_amd/csrc/codec.hpp",
+                               "block_scaled_bit_e2m1_amd/csrc/epilogue.hpp"]}
+MX_PAIRS = [("mxfp4", "mxfp4"), ("mxfp8_e4m3", "mxfp4"), ("mxfp8_e4m3", "mxfp8_e4m3")]
 
 
 def log(msg):
@@ -46,7 +52,7 @@ def log(msg):
 
 def source_sha(kind):
     h = hashlib.sha256()
-    for rel in [KERNEL_SOURCES[kind], "block_scaled_bit_e2m1_amd/csrc/codec.hpp"]:
+    for rel in KERNEL_SOURCES[kind]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -236,7 +242,8 @@ def time_qgemm_mx(device, xfmt, wfmt, m=2048, n=4096, k=4096, reps=100):
     g_ms = graph_event_ms(gemm, 4, reps, device)
     s_ms = graph_event_ms(step, 4, reps // 2, device)
     tf = flops / (g_ms * 1e-3) / 1e12
-    return {"workload": f"qgemm_mx_{xfmt}_x_{wfmt}_{m}x{n}x{k}",
+    name = f"qgemm_mx_{xfmt}_x_{wfmt}_{m}x{n}x{k}"
+    return {"workload": name, "traffic": measured_traffic(name, "qgemm_mx"),
             "note": "scaled-MFMA GEMM, X and W both MX-packed (bsq_qgemm_mx), bf16 out; step = X quantize + GEMM",
             "value": round(tf, 2), "unit": "TFLOP/s", "us_per_launch": round(g_ms * 1e3, 3),
             "peak": peak, "roofline_frac": round(tf / peak, 4), "us_per_step_with_x_quantize": round(s_ms * 1e3, 3)}
@@ -285,6 +292,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only-timed", action="store_true", help="timed workload only (for profiling)")
     ap.add_argument("--mx-only", action="store_true", help="only time the scaled-MFMA GEMMs and exit")
+    ap.add_argument("--mx-pair", default="", help="with --mx-only: one pair XFMT,WFMT (e.g. mxfp4,mxfp4)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="only run torch's copy kernel on MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -311,8 +319,9 @@ def main():
         return
     bsq.lib()
     if args.mx_only:
-        for xf, wf in [("mxfp4", "mxfp4"), ("mxfp8_e4m3", "mxfp4"), ("mxfp8_e4m3", "mxfp8_e4m3")]:
-            print(json.dumps(time_qgemm_mx(device, xf, wf)), flush=True)
+        pairs = [tuple(args.mx_pair.split(","))] if args.mx_pair else MX_PAIRS
+        for xf, wf in pairs:
+            print(json.dumps(time_qgemm_mx(device, xf, wf, reps=max(1, args.steps // 8))), flush=True)
         return
     wl = workloads.WORKLOADS[args.workload]
     kind = "qgemv" if wl.op == "qgemv" else "qgemm"
@@ -366,7 +375,7 @@ def main():
 
     if not args.no_extra and not args.only_timed:
         extra.append(time_quantize(device))
-        for xf, wf in [("mxfp4", "mxfp4"), ("mxfp8_e4m3", "mxfp4"), ("mxfp8_e4m3", "mxfp8_e4m3")]:
+        for xf, wf in MX_PAIRS:
             e = time_qgemm_mx(device, xf, wf)
             extra.append(e)
             log(f"  {e['workload']}: {e['value']:.1f} TFLOP/s ({e['us_per_launch']:.2f} us/launch, "
