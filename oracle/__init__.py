@@ -70,6 +70,10 @@ def lib():
         L.orc_dequant.argtypes = [ctypes.c_int, _i64, _i64, _vp, _vp, _vp, ctypes.c_float, _vp]
         L.orc_matmul.restype = ctypes.c_int
         L.orc_matmul.argtypes = [_vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp, ctypes.c_int]
+        L.orc_matmul_f64.restype = ctypes.c_int
+        L.orc_matmul_f64.argtypes = [_vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp, ctypes.c_int]
+        L.orc_rmsnorm.restype = ctypes.c_int
+        L.orc_rmsnorm.argtypes = [_vp, _vp, _i64, _i64, ctypes.c_double, _vp]
         _lib = L
     return _lib
 
@@ -170,9 +174,25 @@ def dequant_packed(p: dict) -> np.ndarray:
     return dequant(p["fmt"], p["n"], p["k"], p["codes"], p["scales"], p["biases"], p["global"])
 
 
-def matmul(x: np.ndarray, wd: np.ndarray, rows=None, threads: int | None = None):
-    """ref, den (fp64 [len(rows), n]) for rows of X (f32 values) times Wd^T."""
+def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """fp64 [m,k]: x * g / sqrt(mean(x^2) + eps) per row (f32 x and g values)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    m, k = x.shape
+    if g.shape != (k,):
+        raise OracleError("g must have k elements")
+    out = np.empty((m, k), dtype=np.float64)
+    st = lib().orc_rmsnorm(_ptr(x), _ptr(g), m, k, ctypes.c_double(eps), _ptr(out))
+    if st:
+        raise OracleError(f"orc_rmsnorm status {st}")
+    return out
+
+
+def matmul(x: np.ndarray, wd: np.ndarray, rows=None, threads: int | None = None):
+    """ref, den (fp64 [len(rows), n]) for rows of X times Wd^T.  X is taken as
+    f32 values, or as fp64 when it is a float64 array (a normalized activation)."""
+    f64 = x.dtype == np.float64
+    x = np.ascontiguousarray(x, dtype=np.float64 if f64 else np.float32)
     wd = np.ascontiguousarray(wd, dtype=np.float32)
     m, k = x.shape
     n, k2 = wd.shape
@@ -188,7 +208,8 @@ def matmul(x: np.ndarray, wd: np.ndarray, rows=None, threads: int | None = None)
     den = np.empty((nr, n), dtype=np.float64)
     if threads is None:
         threads = max(1, min(16, os.cpu_count() or 1))
-    st = lib().orc_matmul(_ptr(x), _ptr(wd), m, n, k, _ptr(r), nr, _ptr(ref), _ptr(den), threads)
+    fn = lib().orc_matmul_f64 if f64 else lib().orc_matmul
+    st = fn(_ptr(x), _ptr(wd), m, n, k, _ptr(r), nr, _ptr(ref), _ptr(den), threads)
     if st:
         raise OracleError(f"orc_matmul status {st}")
     return ref, den

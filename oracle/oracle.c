@@ -19,6 +19,9 @@
  *   matmul   ref[i,j] = sum_p X[i,p] * Wd[j,p] in fp64, with
  *            den[i,j] = sum_p |X[i,p] * Wd[j,p]| alongside (the
  *            "dequant-then-dot" oracle of PR #250's qgemv / qmm commits).
+ *   rmsnorm  Xhat[i,p] = X[i,p] * g[p] / sqrt(mean_p X[i,p]^2 + eps), the
+ *            activation of the fused RMSNorm + dequantizing GEMV [PR #250,
+ *            commit adding the block-scaled fused RMSNorm + GEMV].
  *
  * All arithmetic is fp64 unless a step fixes a stored precision (f32 scales,
  * bf16 int4 scale/bias).  Readings taken where the pages are silent are
@@ -443,6 +446,7 @@ int orc_dequant(int fmt, int64_t n, int64_t k, const void *codes, const void *sc
 
 struct mm_job {
     const float *x, *wd;
+    const double *xd; /* fp64 X instead of x when not NULL */
     const int64_t *rows;
     int64_t nrows, n, k, r0, r1;
     double *ref, *den;
@@ -452,12 +456,13 @@ static void *mm_worker(void *arg)
 {
     struct mm_job *J = (struct mm_job *)arg;
     for (int64_t r = J->r0; r < J->r1; r++) {
-        const float *xr = J->x + J->rows[r] * J->k;
+        const float *xr = J->xd ? NULL : J->x + J->rows[r] * J->k;
+        const double *xdr = J->xd ? J->xd + J->rows[r] * J->k : NULL;
         for (int64_t j = 0; j < J->n; j++) {
             const float *wr = J->wd + j * J->k;
             double acc = 0.0, mag = 0.0;
             for (int64_t p = 0; p < J->k; p++) {
-                double t = (double)xr[p] * (double)wr[p];
+                double t = (xdr ? xdr[p] : (double)xr[p]) * (double)wr[p];
                 acc += t;
                 mag += fabs(t);
             }
@@ -473,8 +478,8 @@ static void *mm_worker(void *arg)
  *   ref[r,j] = sum_p X[i,p] * Wd[j,p],  den[r,j] = sum_p |X[i,p] * Wd[j,p]|,
  * summed in order of p in fp64.  `rows` may be NULL for all m rows.  Rows
  * are split statically over `threads` workers (no change to any sum). */
-int orc_matmul(const float *x, const float *wd, int64_t m, int64_t n, int64_t k, const int64_t *rows,
-               int64_t nrows, double *ref, double *den, int threads)
+static int matmul_any(const float *x, const double *xd, const float *wd, int64_t m, int64_t n, int64_t k,
+                      const int64_t *rows, int64_t nrows, double *ref, double *den, int threads)
 {
     if (m < 0 || n < 0 || k < 0) return ORC_ERR_ARG;
     int64_t *all = NULL;
@@ -499,7 +504,7 @@ int orc_matmul(const float *x, const float *wd, int64_t m, int64_t n, int64_t k,
         int64_t r0 = t * per, r1 = r0 + per;
         if (r0 > nrows) r0 = nrows;
         if (r1 > nrows) r1 = nrows;
-        jobs[t] = (struct mm_job){x, wd, rows, nrows, n, k, r0, r1, ref, den};
+        jobs[t] = (struct mm_job){x, wd, xd, rows, nrows, n, k, r0, r1, ref, den};
         if (threads == 1)
             mm_worker(&jobs[t]);
         else
@@ -508,5 +513,48 @@ int orc_matmul(const float *x, const float *wd, int64_t m, int64_t n, int64_t k,
     if (threads > 1)
         for (int t = 0; t < threads; t++) pthread_join(tid[t], NULL);
     free(all);
+    return ORC_OK;
+}
+
+int orc_matmul(const float *x, const float *wd, int64_t m, int64_t n, int64_t k, const int64_t *rows,
+               int64_t nrows, double *ref, double *den, int threads)
+{
+    return matmul_any(x, NULL, wd, m, n, k, rows, nrows, ref, den, threads);
+}
+
+/* orc_matmul with an fp64 X [m,k] (used for the normalized activation). */
+int orc_matmul_f64(const double *x, const float *wd, int64_t m, int64_t n, int64_t k, const int64_t *rows,
+                   int64_t nrows, double *ref, double *den, int threads)
+{
+    return matmul_any(NULL, x, wd, m, n, k, rows, nrows, ref, den, threads);
+}
+
+/* ------------------------------------------------------------------------ */
+/* RMSNorm of the activation (fused RMSNorm + dequantizing GEMV).            */
+/* ------------------------------------------------------------------------ */
+
+/* Xhat[i,p] = X[i,p] * g[p] * r_i,  r_i = 1 / sqrt((sum_p X[i,p]^2) / k + eps),
+ * in fp64.  The pages describe the fused op as a first phase that sums x^2
+ * into the row's inverse RMS and a second that accumulates the GEMV over
+ * x * norm_weight * inv_rms [metaltile PR #250, commit adding the block-scaled
+ * fused RMSNorm + dequantizing GEMV]; they print no formula for the inverse
+ * RMS, so the usual one is the reading taken: the mean of squares over the k
+ * elements of the row, eps added inside the square root.  X is [m,k] f32 (bf16
+ * inputs as their exact f32 values), g is [k] f32, Xhat is fp64 [m,k].
+ * k == 0 leaves Xhat empty; eps must be >= 0 and the row must not be all zero
+ * when eps == 0 (ORC_ERR_ARG otherwise). */
+int orc_rmsnorm(const float *x, const float *g, int64_t m, int64_t k, double eps, double *xhat)
+{
+    if (m < 0 || k < 0 || !(eps >= 0.0)) return ORC_ERR_ARG;
+    for (int64_t i = 0; i < m; i++) {
+        const float *xr = x + i * k;
+        double ss = 0.0;
+        for (int64_t p = 0; p < k; p++) ss += (double)xr[p] * (double)xr[p];
+        if (k == 0) continue;
+        const double ms = ss / (double)k + eps;
+        if (!(ms > 0.0)) return ORC_ERR_ARG;
+        const double r = 1.0 / sqrt(ms);
+        for (int64_t p = 0; p < k; p++) xhat[i * k + p] = (double)xr[p] * (double)g[p] * r;
+    }
     return ORC_OK;
 }
