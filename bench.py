@@ -249,6 +249,28 @@ def time_qgemm_mx(device, xfmt, wfmt, m=2048, n=4096, k=4096, reps=100):
             "peak": peak, "roofline_frac": round(tf / peak, 4), "us_per_step_with_x_quantize": round(s_ms * 1e3, 3)}
 
 
+def time_rmsnorm_qgemv(device, fmt="nvfp4", n=4096, k=4096, eps=1e-6):
+    """Fused RMSNorm + decode GEMV (bsq_rmsnorm_qgemv), bf16 x and norm weight,
+    weight copies rotated like the timed GEMV so every launch reads HBM."""
+    import torch
+
+    from block_scaled_bit_e2m1_amd import bsq, workloads
+
+    pw = bsq.pack(fmt, workloads.random_weights(n, k, seed=1001, sigma=0.02))
+    copies = max(1, ROTATE_BYTES // pw.weight_bytes)
+    ws = [bsq.to_device(pw, device) for _ in range(copies)]
+    x = torch.from_numpy(workloads.random_activations(1, k, seed=1002, act="bf16")[0]).to(torch.bfloat16).to(device)
+    g = torch.linspace(0.5, 1.5, k, device=device).to(torch.bfloat16)
+    out = torch.empty((n,), dtype=torch.bfloat16, device=device)
+    it = iter(range(1 << 62))
+    us = graph_event_ms(lambda: bsq.rmsnorm_qgemv(ws[next(it) % copies], x, g, eps, out=out), copies,
+                        max(1, 3000 // copies), device) * 1e3
+    wb = pw.weight_bytes + (4 if fmt == "nvfp4" else 0)
+    return {"workload": f"rmsnorm_qgemv_{fmt}_{n}x{k}", "note": "fused RMSNorm + decode GEMV (bsq_rmsnorm_qgemv)",
+            "value": round(wb / (us * 1e-6) / 1e9, 2), "unit": "GB/s", "us_per_launch": round(us, 3),
+            "roofline_frac": round(wb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def cpu_baseline(wl, budget_s=10.0):
     """The oracle as it stands (dequant, then fp64 dot) on the host cores."""
     import numpy as np
@@ -375,6 +397,9 @@ def main():
 
     if not args.no_extra and not args.only_timed:
         extra.append(time_quantize(device))
+        e = time_rmsnorm_qgemv(device)
+        extra.append(e)
+        log(f"  {e['workload']}: {e['value']:.1f} GB/s ({e['us_per_launch']:.2f} us/launch)")
         for xf, wf in MX_PAIRS:
             e = time_qgemm_mx(device, xf, wf)
             extra.append(e)

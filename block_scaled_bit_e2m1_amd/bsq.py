@@ -32,7 +32,7 @@ PATH_AUTO, PATH_ROWS, PATH_MFMA = 0, 1, 2
 OK, ERR_ARG, ERR_UNSUPPORTED, ERR_SHAPE, ERR_ALIGN, ERR_NONFINITE, ERR_HIP = 0, 1, 2, 3, 4, 5, 6
 
 EXPORTS = ["bsq_packed_bytes", "bsq_pack_host", "bsq_quantize", "bsq_dequant", "bsq_qgemv", "bsq_qgemm", "bsq_qgemm_path",
-           "bsq_qgemm_mx", "bsq_status_string", "bsq_last_error", "bsq_version"]
+           "bsq_qgemm_mx", "bsq_rmsnorm_qgemv", "bsq_status_string", "bsq_last_error", "bsq_version"]
 
 
 class BsqError(RuntimeError):
@@ -60,8 +60,10 @@ def lib() -> ctypes.CDLL:
         L.bsq_qgemv.argtypes = [_c_int, _c_int, _i64, _i64, _vp, _vp, _vp, _f32, _vp, _c_int, _vp, _c_int, _vp]
         L.bsq_qgemm.argtypes = [_c_int, _c_int, _i64, _i64, _i64, _vp, _vp, _vp, _f32, _vp, _c_int, _vp, _c_int, _vp]
         L.bsq_qgemm_path.argtypes = [_c_int] + L.bsq_qgemm.argtypes
+        L.bsq_rmsnorm_qgemv.argtypes = [_c_int, _c_int, _i64, _i64, _i64, _vp, _vp, _vp, _f32, _vp, _vp, _f32, _c_int,
+                                        _vp, _c_int, _vp]
         for f in ("bsq_packed_bytes", "bsq_pack_host", "bsq_quantize", "bsq_dequant", "bsq_qgemv", "bsq_qgemm", "bsq_qgemm_path",
-                  "bsq_qgemm_mx"):
+                  "bsq_qgemm_mx", "bsq_rmsnorm_qgemv"):
             getattr(L, f).restype = _c_int
         for f in ("bsq_status_string", "bsq_last_error", "bsq_version"):
             getattr(L, f).restype = ctypes.c_char_p
@@ -101,6 +103,12 @@ def bsq_qgemv(fmt, block, n, k, codes, scales, biases, global_scale, x, xt, out,
 
 def bsq_qgemm(fmt, block, m, n, k, codes, scales, biases, global_scale, x, xt, out, ot, stream):
     return lib().bsq_qgemm(fmt, block, m, n, k, codes, scales, biases, global_scale, x, xt, out, ot, stream)
+
+
+def bsq_rmsnorm_qgemv(fmt, block, m, n, k, codes, scales, biases, global_scale, x, norm_weight, eps, xt, out, ot,
+                      stream):
+    return lib().bsq_rmsnorm_qgemv(fmt, block, m, n, k, codes, scales, biases, global_scale, x, norm_weight, eps, xt,
+                                   out, ot, stream)
 
 
 def bsq_qgemm_path(path, fmt, block, m, n, k, codes, scales, biases, global_scale, x, xt, out, ot, stream):
@@ -243,6 +251,23 @@ def qgemv(pw: PackedWeight, x: torch.Tensor, out: torch.Tensor | None = None, ou
     st = bsq_qgemv(pw.fmt, 0, pw.n, pw.k, _ptr(pw.codes), _ptr(pw.scales), _ptr(pw.biases), pw.global_scale,
                    _ptr(x), _DT[x.dtype], _ptr(out), _DT[out.dtype], _stream(dev))
     _check(st, "bsq_qgemv")
+    return out
+
+
+def rmsnorm_qgemv(pw: PackedWeight, x: torch.Tensor, norm_weight: torch.Tensor, eps: float,
+                  out: torch.Tensor | None = None, out_dtype=None) -> torch.Tensor:
+    """out = rmsnorm(x, norm_weight, eps) @ dequant(pw)^T, fused (bsq_rmsnorm_qgemv);
+    x is [k] or [m,k], norm_weight [k] of x's dtype."""
+    dev = pw.codes.device
+    x2 = x.reshape(-1, pw.k)
+    if norm_weight.dtype != x.dtype or norm_weight.numel() != pw.k:
+        raise ValueError("norm_weight must be [k] with x's dtype")
+    if out is None:
+        out = torch.empty(tuple(x.shape[:-1]) + (pw.n,), dtype=out_dtype or x.dtype, device=dev)
+    st = bsq_rmsnorm_qgemv(pw.fmt, 0, x2.shape[0], pw.n, pw.k, _ptr(pw.codes), _ptr(pw.scales), _ptr(pw.biases),
+                           pw.global_scale, _ptr(x2), _ptr(norm_weight), float(eps), _DT[x.dtype], _ptr(out),
+                           _DT[out.dtype], _stream(dev))
+    _check(st, "bsq_rmsnorm_qgemv")
     return out
 
 

@@ -198,6 +198,31 @@ bsq_status bsq_qgemm_path(bsq_path path, bsq_format fmt, int block, int64_t m, i
   return matmul(path, fmt, block, m, n, k, codes, scales, biases, global_scale, x, xt, out, ot, stream);
 }
 
+bsq_status bsq_rmsnorm_qgemv(bsq_format fmt, int block, int64_t m, int64_t n, int64_t k, const void *codes,
+                             const void *scales, const void *biases, float global_scale, const void *x,
+                             const void *norm_weight, float eps, bsq_dtype xt, void *out, bsq_dtype ot,
+                             void *stream) {
+  bsq_status s;
+  if ((s = check_format(fmt, block))) return s;
+  if ((s = check_shape(fmt, n, k))) return s;
+  if (m < 0) return fail(BSQ_ERR_ARG, "negative m");
+  if (xt != BSQ_F32 && xt != BSQ_BF16) return fail(BSQ_ERR_ARG, "bad x dtype %d", (int)xt);
+  if (ot != BSQ_F32 && ot != BSQ_BF16) return fail(BSQ_ERR_ARG, "bad out dtype %d", (int)ot);
+  if (!(eps >= 0.0f) || eps > 3.0e38f) return fail(BSQ_ERR_ARG, "eps must be finite and >= 0");
+  if (bsq::is_4bit(fmt) && k % 32) return fail(BSQ_ERR_SHAPE, "k=%lld: 4-bit formats need k %% 32 == 0 here", (long long)k);
+  if (m == 0 || n == 0) return ok();
+  if (!out) return fail(BSQ_ERR_ARG, "null out");
+  if (!aligned(out, ot == BSQ_F32 ? 4 : 2)) return fail(BSQ_ERR_ALIGN, "out misaligned");
+  hipStream_t st = (hipStream_t)stream;
+  if (k == 0) return hip_status(bsq::launch_zero(out, m * n * (ot == BSQ_F32 ? 4 : 2), st), "zero-fill");
+  if ((s = check_weight(fmt, n, k, codes, scales, biases))) return s;
+  if (!x || !norm_weight) return fail(BSQ_ERR_ARG, "null x or norm_weight");
+  if (!aligned(x, 16) || !aligned(norm_weight, 16)) return fail(BSQ_ERR_ALIGN, "x and norm_weight must be 16-byte aligned");
+  if (m > ((int64_t)1 << 40) / k) return fail(BSQ_ERR_SHAPE, "m*k too large");
+  const bsq::QWeight w{(int)fmt, n, k, codes, scales, biases, global_scale};
+  return hip_status(bsq::launch_rows_norm(w, m, x, (int)xt, norm_weight, eps, out, (int)ot, st), "rmsnorm rows launch");
+}
+
 const char *bsq_status_string(bsq_status s) {
   switch (s) {
     case BSQ_OK: return "ok";

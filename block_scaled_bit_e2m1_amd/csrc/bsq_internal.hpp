@@ -48,6 +48,11 @@ struct QWeight {
 hipError_t launch_dequant(const QWeight &w, float *out, hipStream_t s);
 // VALU streaming kernel: any m, f32 or bf16 X (xt/ot: 0 = f32, 1 = bf16).
 hipError_t launch_rows(const QWeight &w, int64_t m, const void *x, int xt, void *out, int ot, hipStream_t s);
+// The same kernel with the fused RMSNorm of each X row: gamma [k] of dtype xt,
+// out = (x * gamma / sqrt(mean(x^2) + eps)) . dequant(W)^T; k % 32 == 0 for
+// 4-bit formats.
+hipError_t launch_rows_norm(const QWeight &w, int64_t m, const void *x, int xt, const void *gam, float eps, void *out,
+                            int ot, hipStream_t s);
 // MFMA kernel: bf16 X, any m >= 1.
 hipError_t launch_mfma(const QWeight &w, int64_t m, const void *x, void *out, int ot, hipStream_t s);
 // Zero-fill an output of `bytes` bytes (k == 0 case).

@@ -23,7 +23,16 @@
 //
 // bf16 X uses the gfx950 conversions (v_cvt_scalef32_pk_bf16_fp4/fp8/bf8 with
 // scale 1.0, which are exact for these element sets) and v_dot2_f32_bf16; f32
-// X and the integer formats use the branch-free software decoders and fp32 FMA.
+// X uses the gfx950 f32 conversions (v_cvt_scalef32_pk_f32_fp4/fp8/bf8) and
+// fp32 FMA; the integer formats use branch-free software decoders.
+//
+// Fused RMSNorm (NORM): the activation is x * g / sqrt(mean(x^2) + eps) per
+// row [metaltile PR #250, commit adding the block-scaled fused RMSNorm +
+// dequantizing GEMV: sum x^2 into the row's inverse RMS, then the GEMV over
+// x * norm_weight * inv_rms].  The inverse RMS is one factor per row, so it
+// comes out of the sum: each wave, which streams the whole row of x anyway,
+// accumulates sum x^2 alongside its dot products over x * g (in f32, for
+// either x dtype) and scales its outputs once at the end; no extra pass.
 #include "bsq_internal.hpp"
 #include "codec.hpp"
 
@@ -47,10 +56,34 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Unscaled element values of one 8-element sub-chunk (software decoders).
+// Unscaled element values of one 8-element sub-chunk: the gfx950 f32
+// conversions for the minifloat elements (scale 1.0: exact, since every E2M1,
+// E4M3 and E5M2 value is an f32), software decoders for the integers.
 template <int F>
 __device__ __forceinline__ void decode8(uint32_t w0, uint32_t w1, float e[8]) {
-  if constexpr (Traits<F>::kBits == 4) {
+  typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+  if constexpr (F == kMXFP4 || F == kNVFP4) {
+    const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w0, 1.0f, 0);
+    const f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w0, 1.0f, 1);
+    const f32x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w0, 1.0f, 2);
+    const f32x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w0, 1.0f, 3);
+    e[0] = p0[0]; e[1] = p0[1]; e[2] = p1[0]; e[3] = p1[1];
+    e[4] = p2[0]; e[5] = p2[1]; e[6] = p3[0]; e[7] = p3[1];
+  } else if constexpr (F == kMXFP8_E4M3 || F == kNVFP8) {
+    const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w0, 1.0f, false);
+    const f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w0, 1.0f, true);
+    const f32x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w1, 1.0f, false);
+    const f32x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w1, 1.0f, true);
+    e[0] = p0[0]; e[1] = p0[1]; e[2] = p1[0]; e[3] = p1[1];
+    e[4] = p2[0]; e[5] = p2[1]; e[6] = p3[0]; e[7] = p3[1];
+  } else if constexpr (F == kMXFP8_E5M2) {
+    const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_bf8(w0, 1.0f, false);
+    const f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_bf8(w0, 1.0f, true);
+    const f32x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_bf8(w1, 1.0f, false);
+    const f32x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_bf8(w1, 1.0f, true);
+    e[0] = p0[0]; e[1] = p0[1]; e[2] = p1[0]; e[3] = p1[1];
+    e[4] = p2[0]; e[5] = p2[1]; e[6] = p3[0]; e[7] = p3[1];
+  } else if constexpr (Traits<F>::kBits == 4) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint32_t c = (w0 >> (4 * i)) & 0xFu;
@@ -136,10 +169,11 @@ __device__ __forceinline__ float scale_value(uint32_t raw) {
 // the round are issued before any arithmetic, so each wave keeps RPW*U HBM
 // requests in flight with no wait between them.  A ragged last round runs
 // the same code with bounds guards.
-template <int F, int M, int XT, bool VEC, int RPW, int U>
+template <int F, int M, int XT, bool VEC, int RPW, int U, bool NORM>
 __global__ void __launch_bounds__(kWaves * 64)
 rows_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, const uint16_t *__restrict__ biases,
-            float global, const void *__restrict__ xv, void *__restrict__ out, int ot, int64_t m, int64_t n, int64_t k) {
+            float global, const void *__restrict__ xv, void *__restrict__ out, int ot, int64_t m, int64_t n, int64_t k,
+            const void *__restrict__ gam, float eps) {
   constexpr int B = Traits<F>::kBlock;
   constexpr int E = Traits<F>::kBits == 4 ? 32 : 16;  // elements per 16-byte chunk
   constexpr int NSUB = E / 8;                           // 8-element sub-chunks per chunk
@@ -160,11 +194,13 @@ rows_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
   for (int mi = 0; mi < M; ++mi) xrow[mi] = (i0 + mi < m ? i0 + mi : m - 1) * k;  // rows past m: valid, unused
 
   for (int64_t j0 = wave * RPW; j0 < n; j0 += nwaves * RPW) {
-    float acc[RPW][M];
+    float acc[RPW][M], ssq[M];
 #pragma unroll
     for (int r = 0; r < RPW; ++r)
 #pragma unroll
       for (int mi = 0; mi < M; ++mi) acc[r][mi] = 0.0f;
+#pragma unroll
+    for (int mi = 0; mi < M; ++mi) ssq[mi] = 0.0f;
     int64_t jr[RPW];
 #pragma unroll
     for (int r = 0; r < RPW; ++r) jr[r] = j0 + r < n ? j0 + r : n - 1;  // rows past n: valid, never stored
@@ -175,6 +211,7 @@ rows_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
       uint4 cw[RPW][U];
       uint32_t sr[RPW][U][NB], br[RPW][U];
       uint4 xq[XPRE ? M : 1][XPRE ? U : 1][XPRE ? NSUB * XW : 1];
+      uint4 gq[NORM && XPRE ? U : 1][NORM && XPRE ? NSUB * XW : 1];  // norm gain of the round
 #pragma unroll
       for (int r = 0; r < RPW; ++r) {
         const uint8_t *crow = codes + jr[r] * row_bytes;
@@ -217,6 +254,22 @@ rows_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
                 xq[mi][u][q] = make_uint4(0, 0, 0, 0);
               }
             }
+        if constexpr (NORM) {
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int q = 0; q < NSUB * XW; ++q) {
+              const int64_t p = kc0 + (int64_t)u * 64 * E + (q / XW) * 8;
+              if (!kG || p < k) {
+                if constexpr (XT == 1)
+                  gq[u][q] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(gam) + p);
+                else
+                  gq[u][q] = reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(gam) + p)[q % XW];
+              } else {
+                gq[u][q] = make_uint4(0, 0, 0, 0);
+              }
+            }
+        }
       }
       // keep every load of the round ahead of the arithmetic
       __builtin_amdgcn_sched_barrier(0);
@@ -254,6 +307,56 @@ rows_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
                 const uint4 *xp = reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(xv) + xrow[mi] + p);
                 xa = xp[0];
                 xb2 = xp[1];
+              }
+              if constexpr (NORM) {
+                // x as f32, its squares into the row's sum, then x * g
+                float xf[8], gf[8];
+                if constexpr (XT == 1) {
+                  const uint32_t xs[4] = {xa.x, xa.y, xa.z, xa.w};
+                  uint4 gv;
+                  if constexpr (XPRE) gv = gq[u][s * XW];
+                  else gv = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(gam) + p);
+                  const uint32_t gs[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+                  for (int i = 0; i < 4; ++i) {
+                    xf[2 * i] = __uint_as_float(xs[i] << 16);
+                    xf[2 * i + 1] = __uint_as_float(xs[i] & 0xFFFF0000u);
+                    gf[2 * i] = __uint_as_float(gs[i] << 16);
+                    gf[2 * i + 1] = __uint_as_float(gs[i] & 0xFFFF0000u);
+                  }
+                } else {
+                  uint4 ga, gb;
+                  if constexpr (XPRE) {
+                    ga = gq[u][s * XW];
+                    gb = gq[u][s * XW + XW - 1];
+                  } else {
+                    const uint4 *gp = reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(gam) + p);
+                    ga = gp[0];
+                    gb = gp[1];
+                  }
+                  const uint32_t xs[8] = {xa.x, xa.y, xa.z, xa.w, xb2.x, xb2.y, xb2.z, xb2.w};
+                  const uint32_t gs[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+#pragma unroll
+                  for (int i = 0; i < 8; ++i) {
+                    xf[i] = __uint_as_float(xs[i]);
+                    gf[i] = __uint_as_float(gs[i]);
+                  }
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                  ssq[mi] = __builtin_fmaf(xf[i], xf[i], ssq[mi]);
+                  xf[i] *= gf[i];
+                }
+#pragma unroll
+                for (int r = 0; r < RPW; ++r) {
+                  const uint32_t cwa[4] = {cw[r][u].x, cw[r][u].y, cw[r][u].z, cw[r][u].w};
+                  const uint32_t w0 = Traits<F>::kBits == 4 ? cwa[s] : cwa[2 * s];
+                  const uint32_t w1 = Traits<F>::kBits == 4 ? 0u : cwa[2 * s + 1];
+                  part[r][mi] = dot8_f32<F>(w0, w1, xf, part[r][mi]);
+                }
+                if constexpr (F == kINT4_AFFINE)
+                  xsum[mi] += ((xf[0] + xf[1]) + (xf[2] + xf[3])) + ((xf[4] + xf[5]) + (xf[6] + xf[7]));
+                continue;
               }
 #pragma unroll
               for (int r = 0; r < RPW; ++r) {
@@ -299,12 +402,16 @@ rows_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
     for (int64_t rr = 0; rr < full_rounds; ++rr) round(std::integral_constant<bool, false>{}, lane0 + rr * per_round);
     if (full_rounds * per_round < k) round(std::integral_constant<bool, true>{}, lane0 + full_rounds * per_round);
 
+    float rinv[M];
+#pragma unroll
+    for (int mi = 0; mi < M; ++mi) rinv[mi] = NORM ? 1.0f / sqrtf(wave_sum(ssq[mi]) / (float)k + eps) : 1.0f;
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
 #pragma unroll
       for (int mi = 0; mi < M; ++mi) {
         float v = wave_sum(acc[r][mi]);
         if constexpr (F == kNVFP4) v *= global;
+        if constexpr (NORM) v *= rinv[mi];
         if (lane == r * M + mi && j0 + r < n && i0 + mi < m) {
           const int64_t o = (i0 + mi) * n + j0 + r;
           if (ot == 0) reinterpret_cast<float *>(out)[o] = v;
@@ -315,8 +422,9 @@ rows_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
   }
 }
 
-template <int F, int M, int XT, int RPW, int U>
-hipError_t run_cfg(const QWeight &w, int64_t m, const void *x, void *out, int ot, hipStream_t s) {
+template <int F, int M, int XT, int RPW, int U, bool NORM>
+hipError_t run_cfg(const QWeight &w, int64_t m, const void *x, void *out, int ot, const void *gam, float eps,
+                   hipStream_t s) {
   const bool vec = Traits<F>::kBits == 8 || (w.k % 32) == 0;  // 16-byte aligned code rows
   const int64_t waves = (w.n + RPW - 1) / RPW;
   int64_t wgs = (waves + kWaves - 1) / kWaves;
@@ -324,11 +432,15 @@ hipError_t run_cfg(const QWeight &w, int64_t m, const void *x, void *out, int ot
   const int64_t ychunks = (m + M - 1) / M;
   const dim3 grid((unsigned)wgs, (unsigned)ychunks);
   if (vec)
-    hipLaunchKernelGGL((rows_kernel<F, M, XT, true, RPW, U>), grid, dim3(kWaves * 64), 0, s, (const uint8_t *)w.codes,
-                       w.scales, (const uint16_t *)w.biases, w.global, x, out, ot, m, w.n, w.k);
+    hipLaunchKernelGGL((rows_kernel<F, M, XT, true, RPW, U, NORM>), grid, dim3(kWaves * 64), 0, s,
+                       (const uint8_t *)w.codes, w.scales, (const uint16_t *)w.biases, w.global, x, out, ot, m, w.n,
+                       w.k, gam, eps);
+  else if constexpr (!NORM)  // the fused RMSNorm requires whole 16-byte code rows (checked by the caller)
+    hipLaunchKernelGGL((rows_kernel<F, M, XT, false, RPW, U, false>), grid, dim3(kWaves * 64), 0, s,
+                       (const uint8_t *)w.codes, w.scales, (const uint16_t *)w.biases, w.global, x, out, ot, m, w.n,
+                       w.k, gam, eps);
   else
-    hipLaunchKernelGGL((rows_kernel<F, M, XT, false, RPW, U>), grid, dim3(kWaves * 64), 0, s, (const uint8_t *)w.codes,
-                       w.scales, (const uint16_t *)w.biases, w.global, x, out, ot, m, w.n, w.k);
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
@@ -337,40 +449,54 @@ hipError_t run_cfg(const QWeight &w, int64_t m, const void *x, void *out, int ot
 // 4-bit codes and two for 8-bit codes (measured best on the 4096x4096 nvfp4
 // and 14336x4096 mxfp8 decode shapes); wider M reuses each decoded chunk M
 // times and keeps one row per wave to bound registers.
-template <int F, int M, int XT>
-hipError_t run_m(const QWeight &w, int64_t m, const void *x, void *out, int ot, hipStream_t s) {
+template <int F, int M, int XT, bool NORM>
+hipError_t run_m(const QWeight &w, int64_t m, const void *x, void *out, int ot, const void *gam, float eps,
+                 hipStream_t s) {
   constexpr int U = Traits<F>::kBits == 4 ? 1 : 2;  // 16-byte chunks per row per round
-  if constexpr (M <= 2 && XT == 1) return run_cfg<F, M, XT, 2, U>(w, m, x, out, ot, s);
-  else return run_cfg<F, M, XT, 1, 2>(w, m, x, out, ot, s);
+  if constexpr (M <= 2 && XT == 1) return run_cfg<F, M, XT, 2, U, NORM>(w, m, x, out, ot, gam, eps, s);
+  else return run_cfg<F, M, XT, 1, 2, NORM>(w, m, x, out, ot, gam, eps, s);
 }
 
-template <int F, int XT>
-hipError_t run_x(const QWeight &w, int64_t m, const void *x, void *out, int ot, hipStream_t s) {
-  if (m <= 1) return run_m<F, 1, XT>(w, m, x, out, ot, s);
-  if (m <= 2) return run_m<F, 2, XT>(w, m, x, out, ot, s);
-  if (m <= 4) return run_m<F, 4, XT>(w, m, x, out, ot, s);
-  return run_m<F, 8, XT>(w, m, x, out, ot, s);
+template <int F, int XT, bool NORM>
+hipError_t run_x(const QWeight &w, int64_t m, const void *x, void *out, int ot, const void *gam, float eps,
+                 hipStream_t s) {
+  if (m <= 1) return run_m<F, 1, XT, NORM>(w, m, x, out, ot, gam, eps, s);
+  if (m <= 2) return run_m<F, 2, XT, NORM>(w, m, x, out, ot, gam, eps, s);
+  if (m <= 4) return run_m<F, 4, XT, NORM>(w, m, x, out, ot, gam, eps, s);
+  return run_m<F, 8, XT, NORM>(w, m, x, out, ot, gam, eps, s);
 }
 
-template <int F>
-hipError_t run_f(const QWeight &w, int64_t m, const void *x, int xt, void *out, int ot, hipStream_t s) {
+template <int F, bool NORM>
+hipError_t run_f(const QWeight &w, int64_t m, const void *x, int xt, void *out, int ot, const void *gam, float eps,
+                 hipStream_t s) {
   if (m > (int64_t)65535 * 8) return hipErrorInvalidValue;
-  return xt == 1 ? run_x<F, 1>(w, m, x, out, ot, s) : run_x<F, 0>(w, m, x, out, ot, s);
+  return xt == 1 ? run_x<F, 1, NORM>(w, m, x, out, ot, gam, eps, s) : run_x<F, 0, NORM>(w, m, x, out, ot, gam, eps, s);
+}
+
+template <bool NORM>
+hipError_t launch(const QWeight &w, int64_t m, const void *x, int xt, void *out, int ot, const void *gam, float eps,
+                  hipStream_t s) {
+  switch (w.fmt) {
+    case kMXFP4: return run_f<kMXFP4, NORM>(w, m, x, xt, out, ot, gam, eps, s);
+    case kNVFP4: return run_f<kNVFP4, NORM>(w, m, x, xt, out, ot, gam, eps, s);
+    case kMXFP8_E4M3: return run_f<kMXFP8_E4M3, NORM>(w, m, x, xt, out, ot, gam, eps, s);
+    case kMXFP8_E5M2: return run_f<kMXFP8_E5M2, NORM>(w, m, x, xt, out, ot, gam, eps, s);
+    case kNVFP8: return run_f<kNVFP8, NORM>(w, m, x, xt, out, ot, gam, eps, s);
+    case kINT4_AFFINE: return run_f<kINT4_AFFINE, NORM>(w, m, x, xt, out, ot, gam, eps, s);
+    case kINT8_SYM: return run_f<kINT8_SYM, NORM>(w, m, x, xt, out, ot, gam, eps, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_rows(const QWeight &w, int64_t m, const void *x, int xt, void *out, int ot, hipStream_t s) {
-  switch (w.fmt) {
-    case kMXFP4: return run_f<kMXFP4>(w, m, x, xt, out, ot, s);
-    case kNVFP4: return run_f<kNVFP4>(w, m, x, xt, out, ot, s);
-    case kMXFP8_E4M3: return run_f<kMXFP8_E4M3>(w, m, x, xt, out, ot, s);
-    case kMXFP8_E5M2: return run_f<kMXFP8_E5M2>(w, m, x, xt, out, ot, s);
-    case kNVFP8: return run_f<kNVFP8>(w, m, x, xt, out, ot, s);
-    case kINT4_AFFINE: return run_f<kINT4_AFFINE>(w, m, x, xt, out, ot, s);
-    case kINT8_SYM: return run_f<kINT8_SYM>(w, m, x, xt, out, ot, s);
-  }
-  return hipErrorInvalidValue;
+  return launch<false>(w, m, x, xt, out, ot, nullptr, 0.0f, s);
+}
+
+hipError_t launch_rows_norm(const QWeight &w, int64_t m, const void *x, int xt, const void *gam, float eps, void *out,
+                            int ot, hipStream_t s) {
+  return launch<true>(w, m, x, xt, out, ot, gam, eps, s);
 }
 
 }  // namespace bsq

@@ -164,6 +164,21 @@ bsq_status bsq_qgemm_path(bsq_path path, bsq_format fmt, int block, int64_t m, i
                           const void *codes, const void *scales, const void *biases, float global_scale,
                           const void *x, bsq_dtype xt, void *out, bsq_dtype ot, void *stream);
 
+/* Fused RMSNorm + GEMV: out[i,j] = r_i * sum_p x[i,p] * g[p] * dequant(W)[j,p],
+ * r_i = 1 / sqrt(mean_p x[i,p]^2 + eps) [metaltile PR #250, commit adding the
+ * block-scaled fused RMSNorm + dequantizing GEMV: phase 1 sums x^2 into the
+ * row's inverse RMS, phase 2 is the GEMV over x * norm_weight * inv_rms; the
+ * mean over k with eps inside the root is this library's reading].  One
+ * streaming pass: the norm is taken alongside the dot products, x * g in f32
+ * for either x dtype.  x: device [m,k] (xt); norm_weight: device [k] of the
+ * same dtype; both 16-byte aligned.  eps: finite, >= 0 (a zero row with
+ * eps == 0 gives NaN).  4-bit formats need k % 32 == 0 (BSQ_ERR_SHAPE).
+ * Weight arguments and out as for bsq_qgemm. */
+bsq_status bsq_rmsnorm_qgemv(bsq_format fmt, int block, int64_t m, int64_t n, int64_t k, const void *codes,
+                             const void *scales, const void *biases, float global_scale, const void *x,
+                             const void *norm_weight, float eps, bsq_dtype xt, void *out, bsq_dtype ot,
+                             void *stream);
+
 /* Static text for a status code. */
 const char *bsq_status_string(bsq_status s);
 

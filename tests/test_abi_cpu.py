@@ -116,3 +116,17 @@ def test_library_pack_equals_oracle_pack_edge_values(orc, fmt):
     w[4, ::2] = 6.0
     w[5] = np.linspace(-7, 7, 256, dtype=np.float32)
     assert _same_pack(orc.pack(fmt, w), bsq.pack(fmt, w))
+
+
+def test_rmsnorm_qgemv_validation():
+    """Argument checks of bsq_rmsnorm_qgemv happen before any launch."""
+    import ctypes as C
+    q = C.c_void_p(256)  # never dereferenced: every call below fails validation first
+    f = bsq.bsq_rmsnorm_qgemv
+    assert f(bsq.MXFP4, 0, 1, 4, 48, q, q, None, 1.0, q, q, 1e-6, bsq.BF16, q, bsq.BF16, None) == bsq.ERR_SHAPE  # k % 32
+    assert f(bsq.MXFP4, 0, 1, 4, 64, q, q, None, 1.0, q, q, -1.0, bsq.BF16, q, bsq.BF16, None) == bsq.ERR_ARG  # eps < 0
+    assert f(bsq.MXFP4, 0, 1, 4, 64, q, q, None, 1.0, q, q, float("nan"), bsq.BF16, q, bsq.BF16, None) == bsq.ERR_ARG
+    assert f(bsq.MXFP4, 0, 1, 4, 64, q, q, None, 1.0, q, None, 1e-6, bsq.BF16, q, bsq.BF16, None) == bsq.ERR_ARG  # no g
+    assert f(bsq.MXFP4, 0, 1, 4, 64, q, q, None, 1.0, q, C.c_void_p(258), 1e-6, bsq.BF16, q, bsq.BF16, None) == bsq.ERR_ALIGN
+    assert f(bsq.MXFP4, 16, 1, 4, 64, q, q, None, 1.0, q, q, 1e-6, bsq.BF16, q, bsq.BF16, None) == bsq.ERR_UNSUPPORTED
+    assert f(bsq.MXFP4, 0, 0, 4, 64, q, q, None, 1.0, q, q, 1e-6, bsq.BF16, q, bsq.BF16, None) == bsq.OK  # m = 0

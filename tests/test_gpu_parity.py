@@ -462,3 +462,50 @@ def test_qgemm_mx_rejects_bad_k():
     q = C.c_void_p(256)  # never dereferenced: validation fails before any launch
     assert bsq.bsq_qgemm_mx(bsq.MXFP8_E4M3, q, q, bsq.MXFP4, q, q, 4, 4, 96, q, bsq.F32, None) == bsq.ERR_SHAPE
     assert bsq.bsq_qgemm_mx(bsq.NVFP4, q, q, bsq.MXFP4, q, q, 4, 4, 128, q, bsq.F32, None) == bsq.ERR_UNSUPPORTED
+
+
+# ----------------------------------------------------------------- fused RMSNorm + GEMV
+def _gain(k, seed, act):
+    g = np.random.default_rng(seed).uniform(0.5, 1.5, k).astype(np.float32)
+    return _bf16_round(g).astype(np.float32) if act == "bf16" else g
+
+
+def _rmsnorm_case(fmt, m, n, k, act, eps, seed, out_dtype=None):
+    W = workloads.random_weights(n, k, seed=seed, sigma=0.02)
+    X = workloads.random_activations(m, k, seed=seed + 1, act=act)
+    g = _gain(k, seed + 2, act)
+    p = oracle.pack(fmt, W)
+    ref, den = oracle.matmul(oracle.rmsnorm(X, g, eps), oracle.dequant_packed(p))
+    pw = bsq.to_device(bsq.pack(fmt, W), DEV)
+    tdt = torch.bfloat16 if act == "bf16" else torch.float32
+    x = torch.from_numpy(X).to(tdt).to(DEV)
+    gt = torch.from_numpy(g).to(tdt).to(DEV)
+    out = bsq.rmsnorm_qgemv(pw, x, gt, eps, out_dtype=out_dtype).float().cpu().numpy()
+    return out, ref, den
+
+
+@pytest.mark.parametrize("fmt", ALL)
+def test_rmsnorm_qgemv_parity(fmt):
+    """Fused RMSNorm + GEMV against oracle rmsnorm -> matmul: bf16 X (bound
+    2e-3) and f32 X (bound 1e-5), m = 1 and 3, ragged n, several rounds of k."""
+    for m, n, k, act, eps in [(1, 300, 1024, "bf16", 1e-6), (3, 129, 512, "f32", 1e-5), (1, 77, 4096, "bf16", 0.0),
+                              (2, 64, 2048, "f32", 0.0)]:
+        out, ref, den = _rmsnorm_case(fmt, m, n, k, act, eps, seed=m * 7 + n)
+        tol = 2e-3 if act == "bf16" else 1e-5
+        check_bound(out, ref, den, tol, f"rmsnorm_qgemv {fmt} m={m} n={n} k={k} {act}", act == "bf16")
+
+
+def test_rmsnorm_qgemv_decode_shape_full():
+    """The decode shape (nvfp4, n = k = 4096, bf16) at full size against the
+    full oracle, and the f32 output of the same launch."""
+    out, ref, den = _rmsnorm_case("nvfp4", 1, 4096, 4096, "bf16", 1e-6, seed=1001)
+    check_bound(out, ref, den, 2e-3, "rmsnorm_qgemv nvfp4 4096", True)
+    out, ref, den = _rmsnorm_case("nvfp4", 1, 4096, 4096, "bf16", 1e-6, seed=1001, out_dtype=torch.float32)
+    check_bound(out, ref, den, 2e-3, "rmsnorm_qgemv nvfp4 4096 f32 out")
+
+
+def test_rmsnorm_qgemv_eps_dominates():
+    """A tiny row with a large eps: the output is the plain GEMV scaled by
+    1/sqrt(eps) (closed form), up to the bf16 bound."""
+    out, ref, den = _rmsnorm_case("mxfp4", 1, 96, 512, "f32", 1e6, seed=3)
+    check_bound(out, ref, den, 1e-5, "rmsnorm_qgemv eps=1e6")
