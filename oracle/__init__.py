@@ -72,6 +72,8 @@ def lib():
         L.orc_matmul.argtypes = [_vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp, ctypes.c_int]
         L.orc_matmul_f64.restype = ctypes.c_int
         L.orc_matmul_f64.argtypes = [_vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp, ctypes.c_int]
+        L.orc_gather_matmul.restype = ctypes.c_int
+        L.orc_gather_matmul.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp]
         L.orc_rmsnorm.restype = ctypes.c_int
         L.orc_rmsnorm.argtypes = [_vp, _vp, _i64, _i64, ctypes.c_double, _vp]
         _lib = L
@@ -186,6 +188,24 @@ def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
     if st:
         raise OracleError(f"orc_rmsnorm status {st}")
     return out
+
+
+def gather_matmul(x: np.ndarray, wd_stack: np.ndarray, ids: np.ndarray, n: int):
+    """ref, den (fp64 [m, n]): row i of X times expert ids[i] of the stack
+    Wd [E*n, k] (rows ids[i]*n .. ids[i]*n + n - 1)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    wd_stack = np.ascontiguousarray(wd_stack, dtype=np.float32)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    m, k = x.shape
+    if wd_stack.shape[1] != k or wd_stack.shape[0] % n or ids.shape != (m,):
+        raise OracleError("shape mismatch")
+    E = wd_stack.shape[0] // n
+    ref = np.empty((m, n), dtype=np.float64)
+    den = np.empty((m, n), dtype=np.float64)
+    st = lib().orc_gather_matmul(_ptr(x), _ptr(wd_stack), _ptr(ids), m, n, k, E, _ptr(ref), _ptr(den))
+    if st:
+        raise OracleError(f"orc_gather_matmul status {st}")
+    return ref, den
 
 
 def matmul(x: np.ndarray, wd: np.ndarray, rows=None, threads: int | None = None):

@@ -22,6 +22,9 @@
  *   rmsnorm  Xhat[i,p] = X[i,p] * g[p] / sqrt(mean_p X[i,p]^2 + eps), the
  *            activation of the fused RMSNorm + dequantizing GEMV [PR #250,
  *            commit adding the block-scaled fused RMSNorm + GEMV].
+ *   gather   ref[i,j] = sum_p X[i,p] * Wd[e_i * n + j, p] for an expert stack
+ *            Wd [E*n, k] and one expert id e_i per row (the expert-routed
+ *            gather qmm of PR #250's MoE commit).
  *
  * All arithmetic is fp64 unless a step fixes a stored precision (f32 scales,
  * bf16 int4 scale/bias).  Readings taken where the pages are silent are
@@ -555,6 +558,39 @@ int orc_rmsnorm(const float *x, const float *g, int64_t m, int64_t k, double eps
         if (!(ms > 0.0)) return ORC_ERR_ARG;
         const double r = 1.0 / sqrt(ms);
         for (int64_t p = 0; p < k; p++) xhat[i * k + p] = (double)xr[p] * (double)g[p] * r;
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Expert-routed matmul (MoE gather).                                        */
+/* ------------------------------------------------------------------------ */
+
+/* ref[i,j] = sum_p X[i,p] * Wd[ids[i]*n + j, p] and den[i,j] = sum_p |...| in
+ * fp64, p in order, for X f32 [m,k] and the dequantized expert stack Wd f32
+ * [E*n, k] [metaltile PR #250, commit adding the per-token expert-routed
+ * matmul: output[m,n] = sum_k dequant(weight[expert_ids[m], n, k]) * x[m,k],
+ * the stack stored as one [E*out_dim, in_dim] tensor so the weight row is
+ * expert_ids[m]*out_dim + n].  An id outside [0, E) is an argument error. */
+int orc_gather_matmul(const float *x, const float *wd, const int32_t *ids, int64_t m, int64_t n, int64_t k,
+                      int64_t E, double *ref, double *den)
+{
+    if (m < 0 || n < 0 || k < 0 || E < 1) return ORC_ERR_ARG;
+    for (int64_t i = 0; i < m; i++)
+        if (ids[i] < 0 || ids[i] >= E) return ORC_ERR_ARG;
+    for (int64_t i = 0; i < m; i++) {
+        const float *xr = x + i * k;
+        for (int64_t j = 0; j < n; j++) {
+            const float *wr = wd + ((int64_t)ids[i] * n + j) * k;
+            double acc = 0.0, mag = 0.0;
+            for (int64_t p = 0; p < k; p++) {
+                const double t = (double)xr[p] * (double)wr[p];
+                acc += t;
+                mag += fabs(t);
+            }
+            ref[i * n + j] = acc;
+            den[i * n + j] = mag;
+        }
     }
     return ORC_OK;
 }
