@@ -271,6 +271,30 @@ def time_rmsnorm_qgemv(device, fmt="nvfp4", n=4096, k=4096, eps=1e-6):
             "roofline_frac": round(wb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def time_gather_qmm(device, fmt="mxfp4", E=8, n=14336, k=4096, ids=(1, 6, 2, 5)):
+    """Expert-routed decode (bsq_gather_qmm): two tokens, top-2 of E experts,
+    bf16 x; three expert stacks rotated so launches read HBM.  Rate = weight
+    bytes of the routed experts per launch / time."""
+    import torch
+
+    from block_scaled_bit_e2m1_amd import bsq, workloads
+
+    pw = bsq.pack(fmt, workloads.random_weights(E * n, k, seed=1005, sigma=0.02))
+    copies = max(1, min(3, ROTATE_BYTES // pw.weight_bytes + 1))
+    stacks = [bsq.to_device(pw, device) for _ in range(copies)]
+    x = torch.from_numpy(workloads.random_activations(len(ids), k, seed=1006, act="bf16")).to(torch.bfloat16).to(device)
+    eids = torch.tensor(ids, dtype=torch.int32, device=device)
+    out = torch.empty((len(ids), n), dtype=torch.bfloat16, device=device)
+    it = iter(range(1 << 62))
+    us = graph_event_ms(lambda: bsq.gather_qmm(stacks[next(it) % copies], E, eids, x, out=out), copies,
+                        max(1, 600 // copies), device) * 1e3
+    wb = len(ids) * pw.weight_bytes // E
+    return {"workload": f"gather_qmm_{fmt}_{E}x{n}x{k}_rows{len(ids)}",
+            "note": "expert-routed decode: each routed row streams its expert (bsq_gather_qmm)",
+            "value": round(wb / (us * 1e-6) / 1e9, 2), "unit": "GB/s", "us_per_launch": round(us, 3),
+            "roofline_frac": round(wb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def cpu_baseline(wl, budget_s=10.0):
     """The oracle as it stands (dequant, then fp64 dot) on the host cores."""
     import numpy as np
@@ -397,9 +421,9 @@ def main():
 
     if not args.no_extra and not args.only_timed:
         extra.append(time_quantize(device))
-        e = time_rmsnorm_qgemv(device)
-        extra.append(e)
-        log(f"  {e['workload']}: {e['value']:.1f} GB/s ({e['us_per_launch']:.2f} us/launch)")
+        for e in (time_rmsnorm_qgemv(device), time_gather_qmm(device)):
+            extra.append(e)
+            log(f"  {e['workload']}: {e['value']:.1f} GB/s ({e['us_per_launch']:.2f} us/launch)")
         for xf, wf in MX_PAIRS:
             e = time_qgemm_mx(device, xf, wf)
             extra.append(e)

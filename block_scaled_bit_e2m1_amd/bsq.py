@@ -32,7 +32,7 @@ PATH_AUTO, PATH_ROWS, PATH_MFMA = 0, 1, 2
 OK, ERR_ARG, ERR_UNSUPPORTED, ERR_SHAPE, ERR_ALIGN, ERR_NONFINITE, ERR_HIP = 0, 1, 2, 3, 4, 5, 6
 
 EXPORTS = ["bsq_packed_bytes", "bsq_pack_host", "bsq_quantize", "bsq_dequant", "bsq_qgemv", "bsq_qgemm", "bsq_qgemm_path",
-           "bsq_qgemm_mx", "bsq_rmsnorm_qgemv", "bsq_status_string", "bsq_last_error", "bsq_version"]
+           "bsq_qgemm_mx", "bsq_rmsnorm_qgemv", "bsq_gather_qmm", "bsq_status_string", "bsq_last_error", "bsq_version"]
 
 
 class BsqError(RuntimeError):
@@ -62,8 +62,10 @@ def lib() -> ctypes.CDLL:
         L.bsq_qgemm_path.argtypes = [_c_int] + L.bsq_qgemm.argtypes
         L.bsq_rmsnorm_qgemv.argtypes = [_c_int, _c_int, _i64, _i64, _i64, _vp, _vp, _vp, _f32, _vp, _vp, _f32, _c_int,
                                         _vp, _c_int, _vp]
+        L.bsq_gather_qmm.argtypes = [_c_int, _c_int, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _f32, _vp, _vp, _c_int, _vp,
+                                     _c_int, _vp, _vp]
         for f in ("bsq_packed_bytes", "bsq_pack_host", "bsq_quantize", "bsq_dequant", "bsq_qgemv", "bsq_qgemm", "bsq_qgemm_path",
-                  "bsq_qgemm_mx", "bsq_rmsnorm_qgemv"):
+                  "bsq_qgemm_mx", "bsq_rmsnorm_qgemv", "bsq_gather_qmm"):
             getattr(L, f).restype = _c_int
         for f in ("bsq_status_string", "bsq_last_error", "bsq_version"):
             getattr(L, f).restype = ctypes.c_char_p
@@ -109,6 +111,12 @@ def bsq_rmsnorm_qgemv(fmt, block, m, n, k, codes, scales, biases, global_scale, 
                       stream):
     return lib().bsq_rmsnorm_qgemv(fmt, block, m, n, k, codes, scales, biases, global_scale, x, norm_weight, eps, xt,
                                    out, ot, stream)
+
+
+def bsq_gather_qmm(fmt, block, m, n, k, num_experts, codes, scales, biases, global_scale, expert_ids, x, xt, out, ot,
+                   status_dev, stream):
+    return lib().bsq_gather_qmm(fmt, block, m, n, k, num_experts, codes, scales, biases, global_scale, expert_ids, x,
+                                xt, out, ot, status_dev, stream)
 
 
 def bsq_qgemm_path(path, fmt, block, m, n, k, codes, scales, biases, global_scale, x, xt, out, ot, stream):
@@ -268,6 +276,25 @@ def rmsnorm_qgemv(pw: PackedWeight, x: torch.Tensor, norm_weight: torch.Tensor, 
                            pw.global_scale, _ptr(x2), _ptr(norm_weight), float(eps), _DT[x.dtype], _ptr(out),
                            _DT[out.dtype], _stream(dev))
     _check(st, "bsq_rmsnorm_qgemv")
+    return out
+
+
+def gather_qmm(stack: PackedWeight, num_experts: int, expert_ids: torch.Tensor, x: torch.Tensor,
+               out: torch.Tensor | None = None, out_dtype=None, status: torch.Tensor | None = None) -> torch.Tensor:
+    """out[i] = x[i] @ dequant(expert expert_ids[i])^T for an expert stack
+    packed as one [num_experts*n, k] weight (bsq_gather_qmm)."""
+    if stack.n % num_experts:
+        raise ValueError("stack rows must be num_experts * n")
+    n = stack.n // num_experts
+    if expert_ids.dtype != torch.int32 or expert_ids.numel() != x.shape[0]:
+        raise ValueError("expert_ids must be int32 with one id per x row")
+    dev = stack.codes.device
+    if out is None:
+        out = torch.empty((x.shape[0], n), dtype=out_dtype or x.dtype, device=dev)
+    st = bsq_gather_qmm(stack.fmt, 0, x.shape[0], n, stack.k, num_experts, _ptr(stack.codes), _ptr(stack.scales),
+                        _ptr(stack.biases), stack.global_scale, _ptr(expert_ids), _ptr(x), _DT[x.dtype], _ptr(out),
+                        _DT[out.dtype], _ptr(status), _stream(dev))
+    _check(st, "bsq_gather_qmm")
     return out
 
 

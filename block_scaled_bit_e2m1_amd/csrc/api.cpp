@@ -223,6 +223,33 @@ bsq_status bsq_rmsnorm_qgemv(bsq_format fmt, int block, int64_t m, int64_t n, in
   return hip_status(bsq::launch_rows_norm(w, m, x, (int)xt, norm_weight, eps, out, (int)ot, st), "rmsnorm rows launch");
 }
 
+bsq_status bsq_gather_qmm(bsq_format fmt, int block, int64_t m, int64_t n, int64_t k, int64_t num_experts,
+                          const void *codes, const void *scales, const void *biases, float global_scale,
+                          const int32_t *expert_ids, const void *x, bsq_dtype xt, void *out, bsq_dtype ot,
+                          int *status_dev, void *stream) {
+  bsq_status s;
+  if ((s = check_format(fmt, block))) return s;
+  if (num_experts < 1) return fail(BSQ_ERR_ARG, "num_experts must be >= 1");
+  if (n < 0 || n > ((int64_t)1 << 40) / num_experts) return fail(BSQ_ERR_SHAPE, "n * num_experts out of range");
+  if ((s = check_shape(fmt, n * num_experts, k))) return s;
+  if (m < 0) return fail(BSQ_ERR_ARG, "negative m");
+  if (m > 65535) return fail(BSQ_ERR_SHAPE, "m=%lld: at most 65535 routed rows per call", (long long)m);
+  if (xt != BSQ_F32 && xt != BSQ_BF16) return fail(BSQ_ERR_ARG, "bad x dtype %d", (int)xt);
+  if (ot != BSQ_F32 && ot != BSQ_BF16) return fail(BSQ_ERR_ARG, "bad out dtype %d", (int)ot);
+  if (m == 0 || n == 0) return ok();
+  if (!out) return fail(BSQ_ERR_ARG, "null out");
+  if (!aligned(out, ot == BSQ_F32 ? 4 : 2)) return fail(BSQ_ERR_ALIGN, "out misaligned");
+  hipStream_t st = (hipStream_t)stream;
+  if (k == 0) return hip_status(bsq::launch_zero(out, m * n * (ot == BSQ_F32 ? 4 : 2), st), "zero-fill");
+  if ((s = check_weight(fmt, n * num_experts, k, codes, scales, biases))) return s;
+  if (!x || !expert_ids) return fail(BSQ_ERR_ARG, "null x or expert_ids");
+  if (!aligned(x, 16) || !aligned(expert_ids, 4)) return fail(BSQ_ERR_ALIGN, "x (16) or expert_ids (4) misaligned");
+  if (status_dev && !aligned(status_dev, 4)) return fail(BSQ_ERR_ALIGN, "status misaligned");
+  const bsq::QWeight w{(int)fmt, n, k, codes, scales, biases, global_scale};
+  return hip_status(bsq::launch_rows_gather(w, m, x, (int)xt, expert_ids, num_experts, status_dev, out, (int)ot, st),
+                    "gather launch");
+}
+
 const char *bsq_status_string(bsq_status s) {
   switch (s) {
     case BSQ_OK: return "ok";

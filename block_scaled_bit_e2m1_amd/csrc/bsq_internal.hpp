@@ -53,6 +53,11 @@ hipError_t launch_rows(const QWeight &w, int64_t m, const void *x, int xt, void 
 // 4-bit formats.
 hipError_t launch_rows_norm(const QWeight &w, int64_t m, const void *x, int xt, const void *gam, float eps, void *out,
                             int ot, hipStream_t s);
+// Expert-routed rows: w is one expert's shape (n rows) over a stacked [E*n, k]
+// weight; X row i uses expert eids[i] (device int32 [m]); a bad id zeroes the
+// row and sets *status (may be null) to 1.
+hipError_t launch_rows_gather(const QWeight &w, int64_t m, const void *x, int xt, const int32_t *eids, int64_t nexp,
+                              int *status, void *out, int ot, hipStream_t s);
 // MFMA kernel: bf16 X, any m >= 1.
 hipError_t launch_mfma(const QWeight &w, int64_t m, const void *x, void *out, int ot, hipStream_t s);
 // Zero-fill an output of `bytes` bytes (k == 0 case).

@@ -33,6 +33,13 @@
 // comes out of the sum: each wave, which streams the whole row of x anyway,
 // accumulates sum x^2 alongside its dot products over x * g (in f32, for
 // either x dtype) and scales its outputs once at the end; no extra pass.
+//
+// Expert routing (eids != null, one X row per launch row): X row i multiplies
+// expert eids[i] of a stacked [E*n, k] weight, i.e. weight rows eids[i]*n ..
+// eids[i]*n + n - 1 [metaltile PR #250, commit adding the per-token
+// expert-routed qmm: one indirection, the stack kept as one packed tensor so
+// nvfp4's single global stays valid].  An id outside [0, E) loads nothing,
+// leaves that output row zero and sets *status to 1 (BSQ_ERR_ARG).
 #include "bsq_internal.hpp"
 #include "codec.hpp"
 
@@ -173,7 +180,8 @@ template <int F, int M, int XT, bool VEC, int RPW, int U, bool NORM>
 __global__ void __launch_bounds__(kWaves * 64)
 rows_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, const uint16_t *__restrict__ biases,
             float global, const void *__restrict__ xv, void *__restrict__ out, int ot, int64_t m, int64_t n, int64_t k,
-            const void *__restrict__ gam, float eps) {
+            const void *__restrict__ gam, float eps, const int32_t *__restrict__ eids, int64_t nexp,
+            int *__restrict__ status) {
   constexpr int B = Traits<F>::kBlock;
   constexpr int E = Traits<F>::kBits == 4 ? 32 : 16;  // elements per 16-byte chunk
   constexpr int NSUB = E / 8;                           // 8-element sub-chunks per chunk
@@ -192,6 +200,15 @@ rows_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
   int64_t xrow[M];
 #pragma unroll
   for (int mi = 0; mi < M; ++mi) xrow[mi] = (i0 + mi < m ? i0 + mi : m - 1) * k;  // rows past m: valid, unused
+  // expert routing: first weight row of this X row's expert (M == 1 here)
+  int64_t jbase = 0;
+  bool skip = false;
+  if (eids) {
+    const int64_t e = eids[i0];
+    skip = e < 0 || e >= nexp;
+    if (skip && status && blockIdx.x == 0 && threadIdx.x == 0) *status = 1;
+    jbase = skip ? 0 : e * n;
+  }
 
   for (int64_t j0 = wave * RPW; j0 < n; j0 += nwaves * RPW) {
     float acc[RPW][M], ssq[M];
@@ -203,7 +220,7 @@ rows_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
     for (int mi = 0; mi < M; ++mi) ssq[mi] = 0.0f;
     int64_t jr[RPW];
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) jr[r] = j0 + r < n ? j0 + r : n - 1;  // rows past n: valid, never stored
+    for (int r = 0; r < RPW; ++r) jr[r] = jbase + (j0 + r < n ? j0 + r : n - 1);  // rows past n: valid, never stored
 
     auto round = [&](auto guard, int64_t kc0) {
       constexpr bool kG = decltype(guard)::value;
@@ -399,8 +416,10 @@ rows_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
     };
 
     const int64_t lane0 = (int64_t)lane * E;
-    for (int64_t rr = 0; rr < full_rounds; ++rr) round(std::integral_constant<bool, false>{}, lane0 + rr * per_round);
-    if (full_rounds * per_round < k) round(std::integral_constant<bool, true>{}, lane0 + full_rounds * per_round);
+    if (!skip) {
+      for (int64_t rr = 0; rr < full_rounds; ++rr) round(std::integral_constant<bool, false>{}, lane0 + rr * per_round);
+      if (full_rounds * per_round < k) round(std::integral_constant<bool, true>{}, lane0 + full_rounds * per_round);
+    }
 
     float rinv[M];
 #pragma unroll
@@ -422,9 +441,16 @@ rows_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
   }
 }
 
+// Routing arguments of a launch (eids == nullptr: no routing).
+struct Route {
+  const int32_t *eids;
+  int64_t nexp;
+  int *status;
+};
+
 template <int F, int M, int XT, int RPW, int U, bool NORM>
 hipError_t run_cfg(const QWeight &w, int64_t m, const void *x, void *out, int ot, const void *gam, float eps,
-                   hipStream_t s) {
+                   const Route &rt, hipStream_t s) {
   const bool vec = Traits<F>::kBits == 8 || (w.k % 32) == 0;  // 16-byte aligned code rows
   const int64_t waves = (w.n + RPW - 1) / RPW;
   int64_t wgs = (waves + kWaves - 1) / kWaves;
@@ -434,11 +460,11 @@ hipError_t run_cfg(const QWeight &w, int64_t m, const void *x, void *out, int ot
   if (vec)
     hipLaunchKernelGGL((rows_kernel<F, M, XT, true, RPW, U, NORM>), grid, dim3(kWaves * 64), 0, s,
                        (const uint8_t *)w.codes, w.scales, (const uint16_t *)w.biases, w.global, x, out, ot, m, w.n,
-                       w.k, gam, eps);
+                       w.k, gam, eps, rt.eids, rt.nexp, rt.status);
   else if constexpr (!NORM)  // the fused RMSNorm requires whole 16-byte code rows (checked by the caller)
     hipLaunchKernelGGL((rows_kernel<F, M, XT, false, RPW, U, false>), grid, dim3(kWaves * 64), 0, s,
                        (const uint8_t *)w.codes, w.scales, (const uint16_t *)w.biases, w.global, x, out, ot, m, w.n,
-                       w.k, gam, eps);
+                       w.k, gam, eps, rt.eids, rt.nexp, rt.status);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -451,39 +477,40 @@ hipError_t run_cfg(const QWeight &w, int64_t m, const void *x, void *out, int ot
 // times and keeps one row per wave to bound registers.
 template <int F, int M, int XT, bool NORM>
 hipError_t run_m(const QWeight &w, int64_t m, const void *x, void *out, int ot, const void *gam, float eps,
-                 hipStream_t s) {
+                 const Route &rt, hipStream_t s) {
   constexpr int U = Traits<F>::kBits == 4 ? 1 : 2;  // 16-byte chunks per row per round
-  if constexpr (M <= 2 && XT == 1) return run_cfg<F, M, XT, 2, U, NORM>(w, m, x, out, ot, gam, eps, s);
-  else return run_cfg<F, M, XT, 1, 2, NORM>(w, m, x, out, ot, gam, eps, s);
+  if constexpr (M <= 2 && XT == 1) return run_cfg<F, M, XT, 2, U, NORM>(w, m, x, out, ot, gam, eps, rt, s);
+  else return run_cfg<F, M, XT, 1, 2, NORM>(w, m, x, out, ot, gam, eps, rt, s);
 }
 
 template <int F, int XT, bool NORM>
 hipError_t run_x(const QWeight &w, int64_t m, const void *x, void *out, int ot, const void *gam, float eps,
-                 hipStream_t s) {
-  if (m <= 1) return run_m<F, 1, XT, NORM>(w, m, x, out, ot, gam, eps, s);
-  if (m <= 2) return run_m<F, 2, XT, NORM>(w, m, x, out, ot, gam, eps, s);
-  if (m <= 4) return run_m<F, 4, XT, NORM>(w, m, x, out, ot, gam, eps, s);
-  return run_m<F, 8, XT, NORM>(w, m, x, out, ot, gam, eps, s);
+                 const Route &rt, hipStream_t s) {
+  if (m <= 1 || rt.eids) return run_m<F, 1, XT, NORM>(w, m, x, out, ot, gam, eps, rt, s);  // routed: a row each
+  if (m <= 2) return run_m<F, 2, XT, NORM>(w, m, x, out, ot, gam, eps, rt, s);
+  if (m <= 4) return run_m<F, 4, XT, NORM>(w, m, x, out, ot, gam, eps, rt, s);
+  return run_m<F, 8, XT, NORM>(w, m, x, out, ot, gam, eps, rt, s);
 }
 
 template <int F, bool NORM>
 hipError_t run_f(const QWeight &w, int64_t m, const void *x, int xt, void *out, int ot, const void *gam, float eps,
-                 hipStream_t s) {
-  if (m > (int64_t)65535 * 8) return hipErrorInvalidValue;
-  return xt == 1 ? run_x<F, 1, NORM>(w, m, x, out, ot, gam, eps, s) : run_x<F, 0, NORM>(w, m, x, out, ot, gam, eps, s);
+                 const Route &rt, hipStream_t s) {
+  if (m > (rt.eids ? (int64_t)65535 : (int64_t)65535 * 8)) return hipErrorInvalidValue;
+  return xt == 1 ? run_x<F, 1, NORM>(w, m, x, out, ot, gam, eps, rt, s)
+                 : run_x<F, 0, NORM>(w, m, x, out, ot, gam, eps, rt, s);
 }
 
 template <bool NORM>
 hipError_t launch(const QWeight &w, int64_t m, const void *x, int xt, void *out, int ot, const void *gam, float eps,
-                  hipStream_t s) {
+                  const Route &rt, hipStream_t s) {
   switch (w.fmt) {
-    case kMXFP4: return run_f<kMXFP4, NORM>(w, m, x, xt, out, ot, gam, eps, s);
-    case kNVFP4: return run_f<kNVFP4, NORM>(w, m, x, xt, out, ot, gam, eps, s);
-    case kMXFP8_E4M3: return run_f<kMXFP8_E4M3, NORM>(w, m, x, xt, out, ot, gam, eps, s);
-    case kMXFP8_E5M2: return run_f<kMXFP8_E5M2, NORM>(w, m, x, xt, out, ot, gam, eps, s);
-    case kNVFP8: return run_f<kNVFP8, NORM>(w, m, x, xt, out, ot, gam, eps, s);
-    case kINT4_AFFINE: return run_f<kINT4_AFFINE, NORM>(w, m, x, xt, out, ot, gam, eps, s);
-    case kINT8_SYM: return run_f<kINT8_SYM, NORM>(w, m, x, xt, out, ot, gam, eps, s);
+    case kMXFP4: return run_f<kMXFP4, NORM>(w, m, x, xt, out, ot, gam, eps, rt, s);
+    case kNVFP4: return run_f<kNVFP4, NORM>(w, m, x, xt, out, ot, gam, eps, rt, s);
+    case kMXFP8_E4M3: return run_f<kMXFP8_E4M3, NORM>(w, m, x, xt, out, ot, gam, eps, rt, s);
+    case kMXFP8_E5M2: return run_f<kMXFP8_E5M2, NORM>(w, m, x, xt, out, ot, gam, eps, rt, s);
+    case kNVFP8: return run_f<kNVFP8, NORM>(w, m, x, xt, out, ot, gam, eps, rt, s);
+    case kINT4_AFFINE: return run_f<kINT4_AFFINE, NORM>(w, m, x, xt, out, ot, gam, eps, rt, s);
+    case kINT8_SYM: return run_f<kINT8_SYM, NORM>(w, m, x, xt, out, ot, gam, eps, rt, s);
   }
   return hipErrorInvalidValue;
 }
@@ -491,12 +518,17 @@ hipError_t launch(const QWeight &w, int64_t m, const void *x, int xt, void *out,
 }  // namespace
 
 hipError_t launch_rows(const QWeight &w, int64_t m, const void *x, int xt, void *out, int ot, hipStream_t s) {
-  return launch<false>(w, m, x, xt, out, ot, nullptr, 0.0f, s);
+  return launch<false>(w, m, x, xt, out, ot, nullptr, 0.0f, Route{nullptr, 0, nullptr}, s);
 }
 
 hipError_t launch_rows_norm(const QWeight &w, int64_t m, const void *x, int xt, const void *gam, float eps, void *out,
                             int ot, hipStream_t s) {
-  return launch<true>(w, m, x, xt, out, ot, gam, eps, s);
+  return launch<true>(w, m, x, xt, out, ot, gam, eps, Route{nullptr, 0, nullptr}, s);
+}
+
+hipError_t launch_rows_gather(const QWeight &w, int64_t m, const void *x, int xt, const int32_t *eids, int64_t nexp,
+                              int *status, void *out, int ot, hipStream_t s) {
+  return launch<false>(w, m, x, xt, out, ot, nullptr, 0.0f, Route{eids, nexp, status}, s);
 }
 
 }  // namespace bsq

@@ -179,6 +179,22 @@ bsq_status bsq_rmsnorm_qgemv(bsq_format fmt, int block, int64_t m, int64_t n, in
                              const void *norm_weight, float eps, bsq_dtype xt, void *out, bsq_dtype ot,
                              void *stream);
 
+/* Expert-routed GEMV rows (MoE gather): out[i,j] = sum_p x[i,p] *
+ * dequant(W)[expert_ids[i]*n + j, p] for a stack of num_experts experts packed
+ * as ONE [num_experts*n, k] weight (layouts as above; nvfp4's global is shared
+ * by all experts) [metaltile PR #250, commit adding the per-token
+ * expert-routed qmm: the weight row is expert_ids[m]*out_dim + n].  Each
+ * routed row streams its own expert's rows (the decode form: one row per
+ * token and chosen expert).  expert_ids: device int32 [m], 4-byte aligned;
+ * x: device [m,k] (xt), 16-byte aligned; out: device [m,n] (ot).  m <= 65535
+ * (BSQ_ERR_SHAPE).  An id outside [0, num_experts) cannot be reported
+ * synchronously: that output row is written as zeros and, if status_dev
+ * (device int, caller-initialised) is given, it is set to BSQ_ERR_ARG. */
+bsq_status bsq_gather_qmm(bsq_format fmt, int block, int64_t m, int64_t n, int64_t k, int64_t num_experts,
+                          const void *codes, const void *scales, const void *biases, float global_scale,
+                          const int32_t *expert_ids, const void *x, bsq_dtype xt, void *out, bsq_dtype ot,
+                          int *status_dev, void *stream);
+
 /* Static text for a status code. */
 const char *bsq_status_string(bsq_status s);
 

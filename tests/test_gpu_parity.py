@@ -509,3 +509,57 @@ def test_rmsnorm_qgemv_eps_dominates():
     1/sqrt(eps) (closed form), up to the bf16 bound."""
     out, ref, den = _rmsnorm_case("mxfp4", 1, 96, 512, "f32", 1e6, seed=3)
     check_bound(out, ref, den, 1e-5, "rmsnorm_qgemv eps=1e6")
+
+
+# ----------------------------------------------------------------- expert-routed gather
+def _gather_case(fmt, E, n, k, ids, act, seed):
+    W = workloads.random_weights(E * n, k, seed=seed, sigma=0.02)
+    X = workloads.random_activations(len(ids), k, seed=seed + 1, act=act)
+    p = oracle.pack(fmt, W)
+    ref, den = oracle.gather_matmul(X, oracle.dequant_packed(p), np.asarray(ids, np.int32), n)
+    stack = bsq.to_device(bsq.PackedWeight(p["fmt"], E * n, k, torch.from_numpy(p["codes"]),
+                                           torch.from_numpy(p["scales"]),
+                                           None if p["biases"] is None else torch.from_numpy(p["biases"]),
+                                           p["global"]), DEV)
+    tdt = torch.bfloat16 if act == "bf16" else torch.float32
+    x = torch.from_numpy(X).to(tdt).to(DEV)
+    eids = torch.tensor(ids, dtype=torch.int32, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = bsq.gather_qmm(stack, E, eids, x, status=status).float().cpu().numpy()
+    return out, ref, den, int(status.item())
+
+
+@pytest.mark.parametrize("fmt", ALL)
+def test_gather_qmm_parity(fmt):
+    """Each row against its expert: 4 experts, repeated and skipped ids,
+    ragged n, bf16 (2e-3) and f32 (1e-5) activations."""
+    for act in ("bf16", "f32"):
+        ids = [2, 0, 2, 3, 3, 0, 2]
+        out, ref, den, st = _gather_case(fmt, 4, 97, 512, ids, act, seed=41)
+        assert st == 0
+        check_bound(out, ref, den, 2e-3 if act == "bf16" else 1e-5, f"gather_qmm {fmt} {act}", act == "bf16")
+
+
+def test_gather_qmm_bad_id_zeroes_row_and_sets_status():
+    ids = [1, 5, 0]  # 5 is outside [0, 4)
+    W = workloads.random_weights(4 * 64, 256, seed=7, sigma=0.02)
+    X = workloads.random_activations(3, 256, seed=8, act="bf16")
+    p = oracle.pack("mxfp4", W)
+    stack = bsq.to_device(bsq.PackedWeight(p["fmt"], 4 * 64, 256, torch.from_numpy(p["codes"]),
+                                           torch.from_numpy(p["scales"]), None, 1.0), DEV)
+    eids = torch.tensor(ids, dtype=torch.int32, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = bsq.gather_qmm(stack, 4, eids, torch.from_numpy(X).to(torch.bfloat16).to(DEV), status=status)
+    out = out.float().cpu().numpy()
+    assert int(status.item()) == bsq.ERR_ARG
+    assert (out[1] == 0).all()
+    good = np.array([0, 2])
+    ref, den = oracle.gather_matmul(X[good], oracle.dequant_packed(p), np.array([1, 0], np.int32), 64)
+    check_bound(out[good], ref, den, 2e-3, "gather_qmm good rows", True)
+
+
+def test_gather_qmm_moe_decode_shape():
+    """8 experts of 1024 x 4096 (mxfp4), two tokens routed top-2."""
+    out, ref, den, st = _gather_case("mxfp4", 8, 1024, 4096, [3, 6, 0, 3], "bf16", seed=1005)
+    assert st == 0
+    check_bound(out, ref, den, 2e-3, "gather_qmm moe decode", True)
