@@ -17,9 +17,12 @@
 //    operands use the same permutation, so the sum is unchanged, and each
 //    lane's weight codes for a step are one contiguous 16-byte (4-bit) or
 //    32-byte (8-bit) run that maps straight onto its B-operand registers.
-//  * X (bf16) goes global -> registers -> LDS (double buffered, rows padded
-//    to 144 bytes so the 16-byte fragment reads are bank-conflict free) and
-//    is read back as A fragments.
+//  * X (bf16) goes global -> registers -> LDS (rows padded to 144 bytes so
+//    the 16-byte fragment reads are bank-conflict free) and is read back as A
+//    fragments.  Large problems use three X buffers and the step-ahead
+//    schedule (SCHED 5): step kt+1 is already in LDS while step kt runs, so
+//    its first fragments and its weight decode happen during step kt and the
+//    MFMAs never wait on the barrier; 8 waves (two per SIMD) per 256x128 tile.
 //  * W codes go global -> registers and are decoded there into bf16 B
 //    fragments, never touching LDS:
 //      mxfp4 / mxfp8:  v_cvt_scalef32_pk_bf16_{fp4,fp8,bf8} with the E8M0
@@ -229,7 +232,9 @@ mfma_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
   constexpr int MT = WTM / 32, NT = WTN / 32;
   constexpr int XCH = BM * (BK / 8) / NTHR;  // 16-byte X chunks per thread per step
   static_assert(XCH * NTHR == BM * (BK / 8), "X tile must split evenly");
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * LDS_LD];
+  // X staging buffers: two, or three for the step-ahead schedule (SCHED 5)
+  constexpr int NBX = SCHED == 5 ? 3 : 2;
+  __shared__ __attribute__((aligned(16))) uint16_t xs[NBX][BM * LDS_LD];
 
   // ---- tile mapping: contiguous tile runs per XCD ----
   const int T = tiles_m * tiles_n;
@@ -384,6 +389,131 @@ mfma_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
   constexpr std::integral_constant<bool, false> kFast{};
   constexpr std::integral_constant<bool, true> kGuarded{};
 
+  if constexpr (SCHED == 5) {
+    // Step-ahead schedule.  Three X buffers: while step kt runs from buffer
+    // kt%3, step kt+1 is already complete in (kt+1)%3 (its first A fragments
+    // are read during step kt's last slice) and step kt+2 is written into
+    // (kt+2)%3 at the end of step kt.  Weights stay in registers: step kt+1's
+    // are decoded during step kt.  Rings: X of step kt+2 in one slot (loaded
+    // a step ahead of its LDS write); W of steps kt+1 .. kt+D, step q in slot
+    // q % D.  So the MFMA stream never waits on the barrier for its first
+    // operands, only on the issue of its own slices.
+    struct SX {
+      uint4 x[XCH];
+    };
+    SX gx;
+    WRaw gw[D][NT];
+    bf16x8_t a0[MT];                       // slice-0 A fragments of the current step
+    bf16x8_t bh[NT][4], bl[NT][4];         // decoded B fragments of the current step
+    auto loadx = [&](auto guard, SX &g, int kt) {
+      constexpr bool kG = decltype(guard)::value;
+      const int64_t k0 = (int64_t)kt * BK;
+      const bool tail = kG && kt >= KF;
+#pragma unroll
+      for (int c = 0; c < XCH; ++c) {
+        if (!kG || !tail || k0 + ((c * NTHR + tid) & 7) * 8 < k) g.x[c] = *reinterpret_cast<const uint4 *>(xp[c] + k0);
+        else g.x[c] = make_uint4(0, 0, 0, 0);
+      }
+    };
+    auto loadw = [&](auto guard, WRaw (&w)[NT], int kt) {
+      constexpr bool kG = decltype(guard)::value;
+      const int64_t kb = (int64_t)kt * BK + 32 * h;
+      const bool tail = kG && kt >= KF;
+#pragma unroll
+      for (int j = 0; j < NT; ++j) load_w<F, VEC>(w[j], codes, scales, biases, wcol[j], k, kb, tail);
+    };
+    auto storex = [&](const SX &g, int buf) {
+#pragma unroll
+      for (int c = 0; c < XCH; ++c) {
+        const int cid = c * NTHR + tid;
+        *reinterpret_cast<uint4 *>(&xs[buf][(cid >> 3) * LDS_LD + (cid & 7) * 8]) = g.x[c];
+      }
+    };
+    auto slice = [&](const bf16x8_t a[MT], int sl) {
+      bf16x8_t bs[NT], ls[NT];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        bs[j] = bh[j][sl];
+        ls[j] = bl[j][sl];
+      }
+      mma(a, bs, ls);
+    };
+    auto step5 = [&](auto guard, int kt, WRaw (&wn)[NT]) {
+      constexpr bool kG = decltype(guard)::value;
+      const bool more = !kG || kt + 1 < KT;
+      const uint16_t *xb = xs[kt % NBX];
+      bf16x8_t a1[MT], bhn[NT][4], bln[NT][4];
+      // slice 0: read slice 1
+      read_a(xb, 1, a1);
+      slice(a0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      // slice 1: read slice 2, decode the next step's weights
+      read_a(xb, 2, a0);
+      if (more) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) decode_w<F>(wn[j], bhn[j], bln[j]);
+      }
+      slice(a1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      // slice 2: read slice 3, refill the weight slot with step kt+1+D
+      read_a(xb, 3, a1);
+      if (!kG || kt + 1 + D < KT) loadw(guard, wn, kt + 1 + D);
+      slice(a0, 2);
+      __builtin_amdgcn_sched_barrier(0);
+      // slice 3: read the next step's slice 0; after the MFMAs, X of step
+      // kt+2 into its buffer and the X slot refilled with step kt+3
+      if (more) read_a(xs[(kt + 1) % NBX], 0, a0);
+      slice(a1, 3);
+      if (!kG || kt + 2 < KT) {
+        storex(gx, (kt + 2) % NBX);
+        if (!kG || kt + 3 < KT) loadx(guard, gx, kt + 3);
+      }
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          bh[j][t] = bhn[j][t];
+          bl[j][t] = bln[j][t];
+        }
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+    };
+
+    // prologue: steps 0 and 1 in LDS, step 2's X in its slot, step 0's
+    // weights decoded, steps 1..D's weights in flight
+    loadx(kGuarded, gx, 0);
+    storex(gx, 0);
+    if (KT > 1) {
+      loadx(kGuarded, gx, 1);
+      storex(gx, 1);
+    }
+    if (KT > 2) loadx(kGuarded, gx, 2);
+    {
+      WRaw w0[NT];
+      loadw(kGuarded, w0, 0);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) decode_w<F>(w0[j], bh[j], bl[j]);
+    }
+#pragma unroll
+    for (int q = 1; q <= D; ++q)
+      if (q < KT) loadw(kGuarded, gw[q % D], q);
+    __syncthreads();
+    read_a(xs[0], 0, a0);
+
+    static_assert(UK % D == 0, "UK must be a multiple of D");
+    constexpr int AHEAD = D + 1 > 3 ? D + 1 : 3;  // furthest step a steady step loads
+    int kt = 0;
+    for (; kt + UK + AHEAD <= KF; kt += UK) {
+#pragma unroll
+      for (int S = 0; S < UK; ++S) step5(kFast, kt + S, gw[(S + 1) % D]);
+    }
+    for (; kt < KT; kt += D) {
+#pragma unroll
+      for (int S = 0; S < D; ++S)
+        if (kt + S < KT) step5(kGuarded, kt + S, gw[(S + 1) % D]);
+    }
+  } else {
+
   // Prologue: steps 0..D-1 in flight, step 0 staged in LDS.
 #pragma unroll
   for (int s = 0; s < D; ++s)
@@ -405,6 +535,8 @@ mfma_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
 #pragma unroll
     for (int S = 0; S < D; ++S)
       if (kt + S < KT) step(kGuarded, kt + S, G[S], G[(S + 1) % D]);
+  }
+
   }
 
   // ---- epilogue ----
@@ -436,11 +568,12 @@ hipError_t run_cfg(const QWeight &w, int64_t m, const void *x, void *out, int ot
 template <int F>
 hipError_t run_f(const QWeight &w, int64_t m, const void *x, void *out, int ot, hipStream_t s) {
   if ((m + 127) / 128 * ((w.n + 63) / 64) > (int64_t)1 << 30) return hipErrorInvalidValue;
-  // 256x128 tiles when they fill the 256 CUs (best measured at m=2048,
-  // n=k=4096); otherwise 128x64 tiles, which run ~3 workgroups per CU and
-  // balance ragged tile counts (best measured at m=512, n=11008, k=4096).
+  // 256x128 tiles with the step-ahead schedule and 8 waves (two per SIMD)
+  // while they give at least half a tile per CU (best measured at m=2048,
+  // n=k=4096 and at m=512, n=11008, k=4096, where 172 such tiles beat 688
+  // 128x64 ones); smaller problems use 128x64 tiles, ~3 workgroups per CU.
   const int64_t big = ((m + 255) / 256) * ((w.n + 127) / 128);
-  if (big >= 256) return run_cfg<F, 256, 128, 2, 2, 2, 4, false, 4>(w, m, x, out, ot, s);
+  if (big >= 128) return run_cfg<F, 256, 128, 2, 4, 1, 4, false, 5>(w, m, x, out, ot, s);
   return run_cfg<F, 128, 64, 2, 2, 2, 4, false, 4>(w, m, x, out, ot, s);
 }
 
