@@ -563,3 +563,51 @@ def test_gather_qmm_moe_decode_shape():
     out, ref, den, st = _gather_case("mxfp4", 8, 1024, 4096, [3, 6, 0, 3], "bf16", seed=1005)
     assert st == 0
     check_bound(out, ref, den, 2e-3, "gather_qmm moe decode", True)
+
+
+def test_new_entry_points_degenerate_shapes():
+    """k = 0 zero-fills (the empty sum); m = 0 / n = 0 launch nothing."""
+    pw = bsq.to_device(bsq.pack("mxfp4", np.ones((32, 64), np.float32)), DEV)
+    empty = bsq.PackedWeight(pw.fmt, 32, 0, pw.codes[:0], pw.scales[:0], None, 1.0)
+    x0 = torch.zeros((2, 0), dtype=torch.bfloat16, device=DEV)
+    out = torch.full((2, 32), 7.0, dtype=torch.bfloat16, device=DEV)
+    st = bsq.bsq_rmsnorm_qgemv(pw.fmt, 0, 2, 32, 0, None, None, None, 1.0, None, None, 1e-6, bsq.BF16,
+                               bsq._ptr(out), bsq.BF16, bsq._stream(DEV))
+    assert st == bsq.OK
+    torch.cuda.synchronize()
+    assert (out == 0).all()
+    st = bsq.bsq_gather_qmm(pw.fmt, 0, 0, 16, 64, 2, bsq._ptr(pw.codes), bsq._ptr(pw.scales), None, 1.0, None, None,
+                            bsq.BF16, None, bsq.BF16, None, bsq._stream(DEV))
+    assert st == bsq.OK
+    del empty, x0
+
+
+def test_new_entry_points_graph_replay():
+    """The fused RMSNorm GEMV and the routed gather captured in a HIP graph:
+    every replay (with eager work between replays) equals the eager result."""
+    W = workloads.random_weights(4 * 96, 512, seed=61, sigma=0.02)
+    pw = bsq.to_device(bsq.pack("nvfp4", W), DEV)
+    x = torch.from_numpy(workloads.random_activations(3, 512, seed=62, act="bf16")).to(torch.bfloat16).to(DEV)
+    g = torch.linspace(0.5, 1.5, 512, device=DEV).to(torch.bfloat16)
+    eids = torch.tensor([3, 0, 3], dtype=torch.int32, device=DEV)
+    ref_n = bsq.rmsnorm_qgemv(pw, x, g, 1e-6).clone()
+    ref_g = bsq.gather_qmm(pw, 4, eids, x).clone()
+    out_n = torch.empty_like(ref_n)
+    out_g = torch.empty_like(ref_g)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        bsq.rmsnorm_qgemv(pw, x, g, 1e-6, out=out_n)
+        bsq.gather_qmm(pw, 4, eids, x, out=out_g)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        bsq.rmsnorm_qgemv(pw, x, g, 1e-6, out=out_n)
+        bsq.gather_qmm(pw, 4, eids, x, out=out_g)
+    for _ in range(3):
+        out_n.fill_(0)
+        out_g.fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_n, ref_n) and torch.equal(out_g, ref_g)
