@@ -82,7 +82,7 @@ struct WRaw {
   uint32_t b0;        // int4 bias bits
 };
 
-template <int F, bool VEC>
+template <int F, bool VEC, bool SC = true>
 __device__ __forceinline__ void load_w(WRaw &r, const uint8_t *__restrict__ codes, const void *__restrict__ scales,
                                        const uint16_t *__restrict__ biases, int64_t col, int64_t k, int64_t kbase,
                                        bool tail) {
@@ -113,6 +113,7 @@ __device__ __forceinline__ void load_w(WRaw &r, const uint8_t *__restrict__ code
       r.c1 = make_uint4(t[4], t[5], t[6], t[7]);
     }
   }
+  if constexpr (!SC) return;
   int64_t b0 = kbase / B, b1 = (kbase + 16) / B;
   if (tail) {
     b0 = b0 < nblk ? b0 : nblk - 1;
@@ -131,6 +132,53 @@ __device__ __forceinline__ void load_w(WRaw &r, const uint8_t *__restrict__ code
     r.s0 = reinterpret_cast<const uint16_t *>(scales)[s + b0];
     r.s1 = r.s0;
     r.b0 = biases[s + b0];
+  }
+}
+
+// Trip scales: one lane's scale (and bias) words for the four 64-k steps of
+// one 256-k trip of its column, loaded with one or two wide loads instead of
+// one small load per step.  Needs k % 256 == 0 (every trip whole and its words
+// aligned).  nvfp8 (64 bytes of f32 scales per trip) keeps per-step loads.
+template <int F> constexpr bool kTripSc = F != kNVFP8;
+template <int F> constexpr int kTripWords =
+    (F == kMXFP4 || F == kMXFP8_E4M3 || F == kMXFP8_E5M2) ? 2 : (F == kNVFP4 || F == kINT4_AFFINE) ? 4 : 8;
+
+template <int F>
+__device__ __forceinline__ void load_trip_sc(uint32_t (&v)[kTripWords<F>], const void *__restrict__ scales,
+                                             const uint16_t *__restrict__ biases, int64_t col, int64_t k, int trip) {
+  constexpr int B = Traits<F>::kBlock, BPT = 256 / B;  // blocks per trip
+  const int64_t blk = col * (k / B) + (int64_t)trip * BPT;
+  if constexpr (F == kMXFP4 || F == kMXFP8_E4M3 || F == kMXFP8_E5M2) {
+    const uint2 t = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint8_t *>(scales) + blk);
+    v[0] = t.x, v[1] = t.y;
+  } else if constexpr (F == kNVFP4) {
+    const uint4 t = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint8_t *>(scales) + blk);
+    v[0] = t.x, v[1] = t.y, v[2] = t.z, v[3] = t.w;
+  } else if constexpr (F == kINT8_SYM) {
+    const uint4 *p = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint32_t *>(scales) + blk);
+    const uint4 a = p[0], b = p[1];
+    v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = b.x, v[5] = b.y, v[6] = b.z, v[7] = b.w;
+  } else if constexpr (F == kINT4_AFFINE) {
+    const uint2 a = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(scales) + blk);
+    const uint2 b = *reinterpret_cast<const uint2 *>(biases + blk);
+    v[0] = a.x, v[1] = a.y, v[2] = b.x, v[3] = b.y;
+  }
+}
+
+// The raw scale fields of step S (0..3) of a trip for lane half h (the lane's
+// k range in that step starts 32h into it).
+template <int F, int S>
+__device__ __forceinline__ void trip_sc(WRaw &r, const uint32_t (&v)[kTripWords<F>], int h) {
+  if constexpr (F == kMXFP4 || F == kMXFP8_E4M3 || F == kMXFP8_E5M2) {
+    r.s0 = (v[S >> 1] >> (8 * (2 * (S & 1) + h))) & 0xFFu;  // block 2S + h
+  } else if constexpr (F == kNVFP4) {
+    r.s0 = (v[S] >> (16 * h)) & 0xFFu;  // blocks 4S + 2h and 4S + 2h + 1
+    r.s1 = (v[S] >> (16 * h + 8)) & 0xFFu;
+  } else if constexpr (F == kINT8_SYM) {
+    r.s0 = h ? v[2 * S + 1] : v[2 * S];  // block 2S + h
+  } else if constexpr (F == kINT4_AFFINE) {
+    r.s0 = (v[S >> 1] >> (16 * (S & 1))) & 0xFFFFu;  // block S
+    r.b0 = (v[2 + (S >> 1)] >> (16 * (S & 1))) & 0xFFFFu;
   }
 }
 
@@ -214,6 +262,16 @@ __device__ __forceinline__ void decode_w(const WRaw &r, bf16x8_t hi[4], bf16x8_t
   }
 }
 
+// Calls fn(integral_constant<int, I>) for I = 0 .. N-1, in order.
+template <int I, int N> struct Unroll {
+  template <class Fn> __device__ __forceinline__ static void run(Fn &&fn) {
+    if constexpr (I < N) {
+      fn(std::integral_constant<int, I>{});
+      Unroll<I + 1, N>::run(fn);
+    }
+  }
+};
+
 // Global data of one BK step held in registers: this thread's X chunks and
 // this lane's weight words for each of its NT column subtiles.
 template <int XCH, int NT>
@@ -222,7 +280,7 @@ struct Slot {
   WRaw w[NT];
 };
 
-template <int F, int BM, int BN, int WGM, int WGN, int D, int UK, bool VEC, bool ROT, int SCHED>
+template <int F, int BM, int BN, int WGM, int WGN, int D, int UK, bool VEC, bool ROT, int SCHED, int DX, bool TS>
 __global__ void __launch_bounds__(WGM *WGN * 64)
 mfma_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, const uint16_t *__restrict__ biases,
             float global, const uint16_t *__restrict__ x, void *__restrict__ out, int ot, int64_t m, int64_t n,
@@ -234,7 +292,10 @@ mfma_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
   static_assert(XCH * NTHR == BM * (BK / 8), "X tile must split evenly");
   // X staging buffers: two, or three for the step-ahead schedule (SCHED 5)
   constexpr int NBX = SCHED == 5 ? 3 : 2;
-  __shared__ __attribute__((aligned(16))) uint16_t xs[NBX][BM * LDS_LD];
+  // one LDS array: the X buffers, reused by the epilogue's staging
+  constexpr int XSZ = NBX * BM * LDS_LD, STG = epi::stage_bytes<WTN, WGM * WGN>() / 2;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[XSZ > STG ? XSZ : STG];
+  auto xs = reinterpret_cast<uint16_t (*)[BM * LDS_LD]>(smem);
 
   // ---- tile mapping: contiguous tile runs per XCD ----
   const int T = tiles_m * tiles_n;
@@ -401,12 +462,23 @@ mfma_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
     struct SX {
       uint4 x[XCH];
     };
-    SX gx;
+    SX gx[DX];
     WRaw gw[D][NT];
+    // trip scales (k % 256 == 0): words of the trip being decoded and of the
+    // next one; step kt decodes step kt+1, so the switch to the next trip
+    // happens in the last step of a trip, which then loads the trip after
+    constexpr bool kTS = TS && kTripSc<F>;
+    static_assert(!kTS || (UK == 4 && !ROT), "trip scales need 4-step trips and no rotation");
+    uint32_t tsc[NT][kTripWords<F>], tsn[NT][kTripWords<F>];
+    const int NTRIP = KT / 4;
     bf16x8_t a0[MT];                       // slice-0 A fragments of the current step
     bf16x8_t bh[NT][4], bl[NT][4];         // decoded B fragments of the current step
     auto loadx = [&](auto guard, SX &g, int kt) {
       constexpr bool kG = decltype(guard)::value;
+      if (ROT) {
+        kt += krot;
+        if (kt >= KT) kt -= KT;
+      }
       const int64_t k0 = (int64_t)kt * BK;
       const bool tail = kG && kt >= KF;
 #pragma unroll
@@ -417,10 +489,18 @@ mfma_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
     };
     auto loadw = [&](auto guard, WRaw (&w)[NT], int kt) {
       constexpr bool kG = decltype(guard)::value;
+      if (ROT) {
+        kt += krot;
+        if (kt >= KT) kt -= KT;
+      }
       const int64_t kb = (int64_t)kt * BK + 32 * h;
       const bool tail = kG && kt >= KF;
 #pragma unroll
-      for (int j = 0; j < NT; ++j) load_w<F, VEC>(w[j], codes, scales, biases, wcol[j], k, kb, tail);
+      for (int j = 0; j < NT; ++j) load_w<F, VEC, !kTS>(w[j], codes, scales, biases, wcol[j], k, kb, tail);
+    };
+    auto loadsc = [&](uint32_t (&v)[NT][kTripWords<F>], int trip) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j) load_trip_sc<F>(v[j], scales, biases, wcol[j], k, trip);
     };
     auto storex = [&](const SX &g, int buf) {
 #pragma unroll
@@ -438,8 +518,9 @@ mfma_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
       }
       mma(a, bs, ls);
     };
-    auto step5 = [&](auto guard, int kt, WRaw (&wn)[NT]) {
+    auto step5 = [&](auto guard, int kt, WRaw (&wn)[NT], SX &xn, auto sidx) {
       constexpr bool kG = decltype(guard)::value;
+      constexpr int SN = (decltype(sidx)::value + 1) % 4;  // step kt+1's place in its trip (kTS)
       const bool more = !kG || kt + 1 < KT;
       const uint16_t *xb = xs[kt % NBX];
       bf16x8_t a1[MT], bhn[NT][4], bln[NT][4];
@@ -451,13 +532,24 @@ mfma_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
       read_a(xb, 2, a0);
       if (more) {
 #pragma unroll
-        for (int j = 0; j < NT; ++j) decode_w<F>(wn[j], bhn[j], bln[j]);
+        for (int j = 0; j < NT; ++j) {
+          if constexpr (kTS) trip_sc<F, SN>(wn[j], SN == 0 ? tsn[j] : tsc[j], h);
+          decode_w<F>(wn[j], bhn[j], bln[j]);
+        }
       }
       slice(a1, 1);
       __builtin_amdgcn_sched_barrier(0);
-      // slice 2: read slice 3, refill the weight slot with step kt+1+D
+      // slice 2: read slice 3, refill the weight slot with step kt+1+D (and,
+      // when step kt+1 opened a trip, move to it and load the trip after)
       read_a(xb, 3, a1);
       if (!kG || kt + 1 + D < KT) loadw(guard, wn, kt + 1 + D);
+      if constexpr (kTS && SN == 0) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+          for (int i = 0; i < kTripWords<F>; ++i) tsc[j][i] = tsn[j][i];
+        if ((kt + 1) / 4 + 1 < NTRIP) loadsc(tsn, (kt + 1) / 4 + 1);
+      }
       slice(a0, 2);
       __builtin_amdgcn_sched_barrier(0);
       // slice 3: read the next step's slice 0; after the MFMAs, X of step
@@ -465,8 +557,8 @@ mfma_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
       if (more) read_a(xs[(kt + 1) % NBX], 0, a0);
       slice(a1, 3);
       if (!kG || kt + 2 < KT) {
-        storex(gx, (kt + 2) % NBX);
-        if (!kG || kt + 3 < KT) loadx(guard, gx, kt + 3);
+        storex(xn, (kt + 2) % NBX);
+        if (!kG || kt + 2 + DX < KT) loadx(guard, xn, kt + 2 + DX);
       }
 #pragma unroll
       for (int j = 0; j < NT; ++j)
@@ -481,18 +573,27 @@ mfma_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
 
     // prologue: steps 0 and 1 in LDS, step 2's X in its slot, step 0's
     // weights decoded, steps 1..D's weights in flight
-    loadx(kGuarded, gx, 0);
-    storex(gx, 0);
+    loadx(kGuarded, gx[0], 0);
+    storex(gx[0], 0);
     if (KT > 1) {
-      loadx(kGuarded, gx, 1);
-      storex(gx, 1);
+      loadx(kGuarded, gx[0], 1);
+      storex(gx[0], 1);
     }
-    if (KT > 2) loadx(kGuarded, gx, 2);
+#pragma unroll
+    for (int q = 2; q < 2 + DX; ++q)
+      if (q < KT) loadx(kGuarded, gx[q % DX], q);
+    if constexpr (kTS) {
+      loadsc(tsc, 0);
+      if (NTRIP > 1) loadsc(tsn, 1);
+    }
     {
       WRaw w0[NT];
       loadw(kGuarded, w0, 0);
 #pragma unroll
-      for (int j = 0; j < NT; ++j) decode_w<F>(w0[j], bh[j], bl[j]);
+      for (int j = 0; j < NT; ++j) {
+        if constexpr (kTS) trip_sc<F, 0>(w0[j], tsc[j], h);
+        decode_w<F>(w0[j], bh[j], bl[j]);
+      }
     }
 #pragma unroll
     for (int q = 1; q <= D; ++q)
@@ -500,17 +601,21 @@ mfma_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
     __syncthreads();
     read_a(xs[0], 0, a0);
 
-    static_assert(UK % D == 0, "UK must be a multiple of D");
-    constexpr int AHEAD = D + 1 > 3 ? D + 1 : 3;  // furthest step a steady step loads
+    static_assert(UK % D == 0 && UK % DX == 0, "UK must be a multiple of D and DX");
+    constexpr int AHEAD = D + 1 > DX + 2 ? D + 1 : DX + 2;  // furthest step a steady step loads
     int kt = 0;
     for (; kt + UK + AHEAD <= KF; kt += UK) {
-#pragma unroll
-      for (int S = 0; S < UK; ++S) step5(kFast, kt + S, gw[(S + 1) % D]);
+      Unroll<0, UK>::run([&](auto S) {
+        constexpr int s_ = decltype(S)::value;
+        step5(kFast, kt + s_, gw[(s_ + 1) % D], gx[(s_ + 2) % DX], S);
+      });
     }
-    for (; kt < KT; kt += D) {
-#pragma unroll
-      for (int S = 0; S < D; ++S)
-        if (kt + S < KT) step5(kGuarded, kt + S, gw[(S + 1) % D]);
+    // drain: kt stays a multiple of UK, so step kt + S uses the slots of S
+    for (; kt < KT; kt += UK) {
+      Unroll<0, UK>::run([&](auto S) {
+        constexpr int s_ = decltype(S)::value;
+        if (kt + s_ < KT) step5(kGuarded, kt + s_, gw[(s_ + 1) % D], gx[(s_ + 2) % DX], S);
+      });
     }
   } else {
 
@@ -542,38 +647,47 @@ mfma_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
   // ---- epilogue ----
   // epilogue: the X buffers are free now; each wave stages its tile there
   // (the nvfp4 global is applied here, once per output)
-  static_assert(epi::stage_bytes<WTN, WGM * WGN>() <= 2 * BM * LDS_LD * 2, "staging must fit in the X buffers");
   __syncthreads();
   epi::store_acc<MT, NT, WTN>(acc, F == kNVFP4 ? global : 1.0f,
-                              reinterpret_cast<uint8_t *>(&xs[0][0]) + wid * 32 * epi::row_stride<WTN, 4>(), lane,
+                              reinterpret_cast<uint8_t *>(smem) + wid * 32 * epi::row_stride<WTN, 4>(), lane,
                               m0 + wm * WTM, n0 + wn * WTN, m, n, out, ot);
 }
 
-template <int F, int BM, int BN, int WGM, int WGN, int D, int UK, bool ROT = false, int SCHED = 1>
+template <int F, int BM, int BN, int WGM, int WGN, int D, int UK, bool ROT = false, int SCHED = 1, int DX = 1>
 hipError_t run_cfg(const QWeight &w, int64_t m, const void *x, void *out, int ot, hipStream_t s) {
   const int tiles_m = (int)((m + BM - 1) / BM), tiles_n = (int)((w.n + BN - 1) / BN);
   const dim3 grid((unsigned)(tiles_m * tiles_n));
   const bool vec = Traits<F>::kBits == 8 || (w.k % 32) == 0;
-  if (vec)
-    hipLaunchKernelGGL((mfma_kernel<F, BM, BN, WGM, WGN, D, UK, true, ROT, SCHED>), grid, dim3(WGM * WGN * 64), 0, s,
-                       (const uint8_t *)w.codes, w.scales, (const uint16_t *)w.biases, w.global, (const uint16_t *)x,
-                       out, ot, m, w.n, w.k, tiles_m, tiles_n);
+  constexpr bool kTripOk = SCHED == 5 && UK == 4 && !ROT && kTripSc<F>;
+  const dim3 block(WGM * WGN * 64);
+  const auto *c = (const uint8_t *)w.codes;
+  const auto *b = (const uint16_t *)w.biases;
+  const auto *xx = (const uint16_t *)x;
+  if (kTripOk && w.k % 256 == 0)
+    hipLaunchKernelGGL((mfma_kernel<F, BM, BN, WGM, WGN, D, UK, true, ROT, SCHED, DX, kTripOk>), grid, block, 0, s, c,
+                       w.scales, b, w.global, xx, out, ot, m, w.n, w.k, tiles_m, tiles_n);
+  else if (vec)
+    hipLaunchKernelGGL((mfma_kernel<F, BM, BN, WGM, WGN, D, UK, true, ROT, SCHED, DX, false>), grid, block, 0, s, c,
+                       w.scales, b, w.global, xx, out, ot, m, w.n, w.k, tiles_m, tiles_n);
   else
-    hipLaunchKernelGGL((mfma_kernel<F, BM, BN, WGM, WGN, D, UK, false, ROT, SCHED>), grid, dim3(WGM * WGN * 64), 0, s,
-                       (const uint8_t *)w.codes, w.scales, (const uint16_t *)w.biases, w.global, (const uint16_t *)x,
-                       out, ot, m, w.n, w.k, tiles_m, tiles_n);
+    hipLaunchKernelGGL((mfma_kernel<F, BM, BN, WGM, WGN, D, UK, false, ROT, SCHED, DX, false>), grid, block, 0, s, c,
+                       w.scales, b, w.global, xx, out, ot, m, w.n, w.k, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
 template <int F>
 hipError_t run_f(const QWeight &w, int64_t m, const void *x, void *out, int ot, hipStream_t s) {
   if ((m + 127) / 128 * ((w.n + 63) / 64) > (int64_t)1 << 30) return hipErrorInvalidValue;
-  // 256x128 tiles with the step-ahead schedule and 8 waves (two per SIMD)
-  // while they give at least half a tile per CU (best measured at m=2048,
-  // n=k=4096 and at m=512, n=11008, k=4096, where 172 such tiles beat 688
-  // 128x64 ones); smaller problems use 128x64 tiles, ~3 workgroups per CU.
-  const int64_t big = ((m + 255) / 256) * ((w.n + 127) / 128);
-  if (big >= 128) return run_cfg<F, 256, 128, 2, 4, 1, 4, false, 5>(w, m, x, out, ot, s);
+  // Step-ahead schedule, 8 waves (two per SIMD), while the tiling gives at
+  // least half a tile per CU: 128x256 tiles (one wave per 32 columns, all
+  // 128 rows) first, as a 128-row X tile plus 256 weight columns is the
+  // least global data per flop (measured at m=2048, n=k=4096: 63 vs 68 us for
+  // 256x128; at m=512, n=11008, k=4096: 101-103 vs 106 us); then 256x128;
+  // smaller problems use 128x64 tiles, ~3 workgroups per CU.
+  const int64_t wide = ((m + 127) / 128) * ((w.n + 255) / 256);
+  const int64_t tall = ((m + 255) / 256) * ((w.n + 127) / 128);
+  if (w.n >= 256 && wide >= 128) return run_cfg<F, 128, 256, 1, 8, 1, 4, false, 5>(w, m, x, out, ot, s);
+  if (tall >= 128) return run_cfg<F, 256, 128, 2, 4, 1, 4, false, 5>(w, m, x, out, ot, s);
   return run_cfg<F, 128, 64, 2, 2, 2, 4, false, 4>(w, m, x, out, ot, s);
 }
 

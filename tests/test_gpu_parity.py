@@ -194,6 +194,32 @@ def test_qgemm_mfma_parity(fmt):
 
 
 @pytest.mark.parametrize("fmt", ALL)
+def test_qgemm_mfma_wide_tiles(fmt):
+    """Problems with at least 128 tiles of 128x256 (the wide tiling): k a
+    multiple of 256 (scales loaded per 256-k trip: one trip, several trips and
+    the guarded drain), k not a multiple of 256 (per-step scale loads), ragged
+    m and n, f32 output, and for nvfp4 k not a multiple of 32.  Rows sampled
+    across the 128-row tiles; every column checked."""
+    cases = [(1000, 4100, 512, torch.bfloat16), (1024, 4096, 256, torch.float32), (1030, 4096, 320, torch.bfloat16),
+             (1024, 4096, 2048 + 256, torch.bfloat16)]
+    if fmt == "nvfp4":
+        cases.append((1024, 4096, 272, torch.bfloat16))
+    rng = np.random.default_rng(77)
+    for m, n, k, od in cases:
+        if k % BLOCK[fmt]:
+            continue
+        W = workloads.random_weights(n, k, seed=m + k, sigma=0.02, outliers=True)
+        X = workloads.random_activations(m, k, seed=m + k + 1)
+        p, d = packed(fmt, W)
+        xt = torch.from_numpy(X).to(torch.bfloat16).to(DEV)
+        out = bsq.qgemm(d, xt, out_dtype=od, path=bsq.PATH_MFMA).float().cpu().numpy()
+        rows = np.unique(np.concatenate([[0, 127, 128, 255, m - 1], rng.choice(m, 27, replace=False)]))
+        ref, den = oracle.matmul(X, oracle.dequant_packed(p), rows=rows)
+        check_bound(out[rows], ref, den, 2e-3, f"mfma wide {fmt} m={m} n={n} k={k}", od == torch.bfloat16)
+        assert np.isfinite(out).all()
+
+
+@pytest.mark.parametrize("fmt", ALL)
 def test_mfma_f32_output(fmt):
     out, ref, den, b = run_matmul(fmt, 64, 96, 256, "bf16", bsq.PATH_MFMA, seed=11, out_dtype=torch.float32)
     assert not b
