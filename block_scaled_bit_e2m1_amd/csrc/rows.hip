@@ -49,6 +49,7 @@ namespace bsq {
 namespace {
 
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2_t, u); }
 
@@ -237,7 +238,15 @@ rows_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
           const int64_t kc = kc0 + (int64_t)u * 64 * E;
           const int64_t off = Traits<F>::kBits == 4 ? kc / 2 : kc;
           if (!kG) {
-            cw[r][u] = *reinterpret_cast<const uint4 *>(crow + off);
+            // bf16 X (decode and m <= 8: one X chunk per launch) reads each
+            // weight byte once: a streaming (nontemporal) load, measured 5-8%
+            // faster on the decode shapes; f32 X chunks re-read the rows
+            if constexpr (XT == 1) {
+              const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(crow + off));
+              cw[r][u] = make_uint4(t.x, t.y, t.z, t.w);
+            } else {
+              cw[r][u] = *reinterpret_cast<const uint4 *>(crow + off);
+            }
           } else {
             uint32_t t[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
