@@ -55,6 +55,15 @@ constexpr int BK = 64;
 constexpr int LDS_LD = BK + 8;  // bf16 per LDS row: 128 data bytes + 16 pad
 
 template <int F> constexpr bool kSplit = (F == kNVFP8 || F == kINT8_SYM || F == kINT4_AFFINE);
+// int8 in the step-ahead kernel instead: the integer codes go to the MFMA as
+// they are (bf16 holds every q in [-128, 127] exactly), a per-block partial sum
+// P is formed in fp32 and the block's scale is applied to P once, not per
+// element ("fold in that block's scale ONCE", rlx-cpu quant.rs
+// dequant_matmul_int8): acc += s_blk * P_blk.  One MFMA per slice instead of
+// the hi + lo pair.  (int4's bias term would need per-row X sums of every
+// group beside the partial sums; at two waves per SIMD that does not fit in
+// the register file, so int4 keeps hi + lo.)
+template <int F> constexpr bool kFold = (F == kINT8_SYM);
 
 __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
   const bf16x2_t v = {(__bf16)a, (__bf16)b};  // round to nearest even
@@ -82,7 +91,7 @@ struct WRaw {
   uint32_t b0;        // int4 bias bits
 };
 
-template <int F, bool VEC, bool SC = true>
+template <int F, bool VEC, bool SC = true, bool P2 = false>
 __device__ __forceinline__ void load_w(WRaw &r, const uint8_t *__restrict__ codes, const void *__restrict__ scales,
                                        const uint16_t *__restrict__ biases, int64_t col, int64_t k, int64_t kbase,
                                        bool tail) {
@@ -101,20 +110,25 @@ __device__ __forceinline__ void load_w(WRaw &r, const uint8_t *__restrict__ code
     }
     r.c1 = make_uint4(0, 0, 0, 0);
   } else {
+    // P2: the lane's two 16-byte runs are 32 bytes apart (k0+16h and k0+32+16h)
+    constexpr int O1 = P2 ? 32 : 16;
     const uint8_t *p = codes + col * k + kbase;
     if (!tail) {
-      r.c0 = reinterpret_cast<const uint4 *>(p)[0];
-      r.c1 = reinterpret_cast<const uint4 *>(p)[1];
+      r.c0 = *reinterpret_cast<const uint4 *>(p);
+      r.c1 = *reinterpret_cast<const uint4 *>(p + O1);
     } else {
       uint32_t t[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) t[q] = (kbase + 4 * q < k) ? reinterpret_cast<const uint32_t *>(p)[q] : 0u;
+      for (int q = 0; q < 8; ++q) {
+        const int off = q < 4 ? 4 * q : O1 + 4 * (q - 4);
+        t[q] = (kbase + off < k) ? *reinterpret_cast<const uint32_t *>(p + off) : 0u;
+      }
       r.c0 = make_uint4(t[0], t[1], t[2], t[3]);
       r.c1 = make_uint4(t[4], t[5], t[6], t[7]);
     }
   }
   if constexpr (!SC) return;
-  int64_t b0 = kbase / B, b1 = (kbase + 16) / B;
+  int64_t b0 = kbase / B, b1 = (kbase + (P2 ? 32 : 16)) / B;
   if (tail) {
     b0 = b0 < nblk ? b0 : nblk - 1;
     b1 = b1 < nblk ? b1 : nblk - 1;
@@ -127,7 +141,7 @@ __device__ __forceinline__ void load_w(WRaw &r, const uint8_t *__restrict__ code
   } else if constexpr (F == kNVFP8 || F == kINT8_SYM) {
     const uint32_t *sp = reinterpret_cast<const uint32_t *>(scales) + s;
     r.s0 = sp[b0];
-    r.s1 = (B == 16) ? sp[b1] : r.s0;
+    r.s1 = (B == 16 || P2) ? sp[b1] : r.s0;
   } else {
     r.s0 = reinterpret_cast<const uint16_t *>(scales)[s + b0];
     r.s1 = r.s0;
@@ -139,7 +153,7 @@ __device__ __forceinline__ void load_w(WRaw &r, const uint8_t *__restrict__ code
 // one 256-k trip of its column, loaded with one or two wide loads instead of
 // one small load per step.  Needs k % 256 == 0 (every trip whole and its words
 // aligned).  nvfp8 (64 bytes of f32 scales per trip) keeps per-step loads.
-template <int F> constexpr bool kTripSc = F != kNVFP8;
+template <int F> constexpr bool kTripSc = F != kNVFP8 && !kFold<F>;
 template <int F> constexpr int kTripWords =
     (F == kMXFP4 || F == kMXFP8_E4M3 || F == kMXFP8_E5M2) ? 2 : (F == kNVFP4 || F == kINT4_AFFINE) ? 4 : 8;
 
@@ -167,13 +181,16 @@ __device__ __forceinline__ void load_trip_sc(uint32_t (&v)[kTripWords<F>], const
 
 // The raw scale fields of step S (0..3) of a trip for lane half h (the lane's
 // k range in that step starts 32h into it).
-template <int F, int S>
+template <int F, int S, bool FOLD = false>
 __device__ __forceinline__ void trip_sc(WRaw &r, const uint32_t (&v)[kTripWords<F>], int h) {
   if constexpr (F == kMXFP4 || F == kMXFP8_E4M3 || F == kMXFP8_E5M2) {
     r.s0 = (v[S >> 1] >> (8 * (2 * (S & 1) + h))) & 0xFFu;  // block 2S + h
   } else if constexpr (F == kNVFP4) {
     r.s0 = (v[S] >> (16 * h)) & 0xFFu;  // blocks 4S + 2h and 4S + 2h + 1
     r.s1 = (v[S] >> (16 * h + 8)) & 0xFFu;
+  } else if constexpr (F == kINT8_SYM && FOLD) {
+    r.s0 = v[2 * S];  // both blocks of the step, for every lane
+    r.s1 = v[2 * S + 1];
   } else if constexpr (F == kINT8_SYM) {
     r.s0 = h ? v[2 * S + 1] : v[2 * S];  // block 2S + h
   } else if constexpr (F == kINT4_AFFINE) {
@@ -183,10 +200,22 @@ __device__ __forceinline__ void trip_sc(WRaw &r, const uint32_t (&v)[kTripWords<
 }
 
 // Build the B fragments (hi, and lo for split formats) of the 4 k-slices.
-template <int F>
-__device__ __forceinline__ void decode_w(const WRaw &r, bf16x8_t hi[4], bf16x8_t lo[4]) {
+// FOLD (int8): the integer codes as bf16 (exact) and the step's fold factors
+// fs: the scales of its two 32-blocks.
+template <int F, bool FOLD = false>
+__device__ __forceinline__ void decode_w(const WRaw &r, bf16x8_t hi[4], bf16x8_t lo[4], float fs[2] = nullptr) {
   const uint32_t cw[8] = {r.c0.x, r.c0.y, r.c0.z, r.c0.w, r.c1.x, r.c1.y, r.c1.z, r.c1.w};
-  if constexpr (F == kMXFP4) {
+  if constexpr (FOLD && F == kINT8_SYM) {
+    fs[0] = __uint_as_float(r.s0);
+    fs[1] = __uint_as_float(r.s1);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float q[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[i] = (float)(int)(int8_t)(uint8_t)(cw[2 * t + (i >> 2)] >> (8 * (i & 3)));
+      hi[t] = frag(pk_bf16(q[0], q[1]), pk_bf16(q[2], q[3]), pk_bf16(q[4], q[5]), pk_bf16(q[6], q[7]));
+    }
+  } else if constexpr (F == kMXFP4) {
     const float sc = __uint_as_float(r.s0 << 23);  // exponent-only scale operand
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -292,6 +321,12 @@ mfma_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
   static_assert(XCH * NTHR == BM * (BK / 8), "X tile must split evenly");
   // X staging buffers: two, or three for the step-ahead schedule (SCHED 5)
   constexpr int NBX = SCHED == 5 ? 3 : 2;
+  // int8 fold (step-ahead schedule; the small-problem schedule keeps hi + lo)
+  constexpr bool FOLD = kFold<F> && SCHED == 5;
+  constexpr bool SPLIT = kSplit<F> && !FOLD;
+  // int8 fold: slice t, lane half h covers k = 32(t/2) + 16h + 8(t%2) + 0..7, so
+  // slices 0,1 hold block 2kt and slices 2,3 block 2kt+1 (each MFMA one block)
+  constexpr bool P2 = FOLD && Traits<F>::kBits == 8;
   // one LDS array: the X buffers, reused by the epilogue's staging
   constexpr int XSZ = NBX * BM * LDS_LD, STG = epi::stage_bytes<WTN, WGM * WGN>() / 2;
   __shared__ __attribute__((aligned(16))) uint16_t smem[XSZ > STG ? XSZ : STG];
@@ -371,9 +406,10 @@ mfma_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
   // One k step: decode this step's weights, refill the slot with step kt + D,
   // multiply from LDS, stage step kt + 1 into the other LDS buffer.
   auto read_a = [&](const uint16_t *xb, int s, bf16x8_t a[MT]) {
+    const int ko = P2 ? 32 * (s >> 1) + 16 * h + 8 * (s & 1) : 32 * h + 8 * s;
 #pragma unroll
     for (int i = 0; i < MT; ++i)
-      a[i] = *reinterpret_cast<const bf16x8_t *>(&xb[(wm * WTM + i * 32 + l32) * LDS_LD + 32 * h + 8 * s]);
+      a[i] = *reinterpret_cast<const bf16x8_t *>(&xb[(wm * WTM + i * 32 + l32) * LDS_LD + ko]);
   };
   auto mma = [&](const bf16x8_t a[MT], const bf16x8_t bh[NT], const bf16x8_t bl[NT]) {
 #pragma unroll
@@ -381,7 +417,7 @@ mfma_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bh[j], acc[i][j], 0, 0, 0);
-        if constexpr (kSplit<F>) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bl[j], acc[i][j], 0, 0, 0);
+        if constexpr (SPLIT) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bl[j], acc[i][j], 0, 0, 0);
       }
   };
   auto step = [&](auto guard, int kt, Slot<XCH, NT> &cur, const Slot<XCH, NT> &nxt) {
@@ -473,6 +509,9 @@ mfma_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
     const int NTRIP = KT / 4;
     bf16x8_t a0[MT];                       // slice-0 A fragments of the current step
     bf16x8_t bh[NT][4], bl[NT][4];         // decoded B fragments of the current step
+    float fs[NT][2], fsn[NT][2];           // fold factors of the current and next step (FOLD)
+    f32x16_t pacc[MT][NT];                 // per-block partial sums (FOLD)
+    const f32x16_t kZero = {};
     auto loadx = [&](auto guard, SX &g, int kt) {
       constexpr bool kG = decltype(guard)::value;
       if (ROT) {
@@ -493,10 +532,10 @@ mfma_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
         kt += krot;
         if (kt >= KT) kt -= KT;
       }
-      const int64_t kb = (int64_t)kt * BK + 32 * h;
+      const int64_t kb = (int64_t)kt * BK + (P2 ? 16 : 32) * h;
       const bool tail = kG && kt >= KF;
 #pragma unroll
-      for (int j = 0; j < NT; ++j) load_w<F, VEC, !kTS>(w[j], codes, scales, biases, wcol[j], k, kb, tail);
+      for (int j = 0; j < NT; ++j) load_w<F, VEC, !kTS, P2>(w[j], codes, scales, biases, wcol[j], k, kb, tail);
     };
     auto loadsc = [&](uint32_t (&v)[NT][kTripWords<F>], int trip) {
 #pragma unroll
@@ -509,7 +548,32 @@ mfma_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
         *reinterpret_cast<uint4 *>(&xs[buf][(cid >> 3) * LDS_LD + (cid & 7) * 8]) = g.x[c];
       }
     };
-    auto slice = [&](const bf16x8_t a[MT], int sl) {
+    auto slice = [&](const bf16x8_t a[MT], auto SL) {
+      constexpr int sl = decltype(SL)::value;
+      if constexpr (FOLD) {
+        constexpr bool first = P2 ? (sl & 1) == 0 : sl == 0;
+        constexpr bool last = P2 ? (sl & 1) == 1 : sl == 3;
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+          for (int j = 0; j < NT; ++j) {
+            if constexpr (first)
+              pacc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bh[j][sl], kZero, 0, 0, 0);
+            else
+              pacc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bh[j][sl], pacc[i][j], 0, 0, 0);
+          }
+        if constexpr (last) {
+#pragma unroll
+          for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+              const float sc = P2 ? fs[j][sl >> 1] : fs[j][0];
+#pragma unroll
+              for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_fmaf(pacc[i][j][v], sc, acc[i][j][v]);
+            }
+        }
+        return;
+      }
       bf16x8_t bs[NT], ls[NT];
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
@@ -526,22 +590,28 @@ mfma_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
       bf16x8_t a1[MT], bhn[NT][4], bln[NT][4];
       // slice 0: read slice 1
       read_a(xb, 1, a1);
-      slice(a0, 0);
+      slice(a0, std::integral_constant<int, 0>{});
       __builtin_amdgcn_sched_barrier(0);
-      // slice 1: read slice 2, decode the next step's weights
-      read_a(xb, 2, a0);
-      if (more) {
+      // slice 1: read slice 2, decode the next step's weights (int8 fold: in
+      // slice 2, where fewer registers are live than beside its first block fold)
+      constexpr int kDec = FOLD ? 2 : 1;
+      auto decode_next = [&]() {
+        if (more) {
 #pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          if constexpr (kTS) trip_sc<F, SN>(wn[j], SN == 0 ? tsn[j] : tsc[j], h);
-          decode_w<F>(wn[j], bhn[j], bln[j]);
+          for (int j = 0; j < NT; ++j) {
+            if constexpr (kTS) trip_sc<F, SN, FOLD>(wn[j], SN == 0 ? tsn[j] : tsc[j], h);
+            decode_w<F, FOLD>(wn[j], bhn[j], bln[j], fsn[j]);
+          }
         }
-      }
-      slice(a1, 1);
+      };
+      read_a(xb, 2, a0);
+      if constexpr (kDec == 1) decode_next();
+      slice(a1, std::integral_constant<int, 1>{});
       __builtin_amdgcn_sched_barrier(0);
       // slice 2: read slice 3, refill the weight slot with step kt+1+D (and,
       // when step kt+1 opened a trip, move to it and load the trip after)
       read_a(xb, 3, a1);
+      if constexpr (kDec == 2) decode_next();
       if (!kG || kt + 1 + D < KT) loadw(guard, wn, kt + 1 + D);
       if constexpr (kTS && SN == 0) {
 #pragma unroll
@@ -550,23 +620,26 @@ mfma_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
           for (int i = 0; i < kTripWords<F>; ++i) tsc[j][i] = tsn[j][i];
         if ((kt + 1) / 4 + 1 < NTRIP) loadsc(tsn, (kt + 1) / 4 + 1);
       }
-      slice(a0, 2);
+      slice(a0, std::integral_constant<int, 2>{});
       __builtin_amdgcn_sched_barrier(0);
       // slice 3: read the next step's slice 0; after the MFMAs, X of step
       // kt+2 into its buffer and the X slot refilled with step kt+3
       if (more) read_a(xs[(kt + 1) % NBX], 0, a0);
-      slice(a1, 3);
+      slice(a1, std::integral_constant<int, 3>{});
       if (!kG || kt + 2 < KT) {
         storex(xn, (kt + 2) % NBX);
         if (!kG || kt + 2 + DX < KT) loadx(guard, xn, kt + 2 + DX);
       }
 #pragma unroll
-      for (int j = 0; j < NT; ++j)
+      for (int j = 0; j < NT; ++j) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           bh[j][t] = bhn[j][t];
           bl[j][t] = bln[j][t];
         }
+        fs[j][0] = fsn[j][0];
+        fs[j][1] = fsn[j][1];
+      }
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
     };
@@ -591,8 +664,8 @@ mfma_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
       loadw(kGuarded, w0, 0);
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        if constexpr (kTS) trip_sc<F, 0>(w0[j], tsc[j], h);
-        decode_w<F>(w0[j], bh[j], bl[j]);
+        if constexpr (kTS) trip_sc<F, 0, FOLD>(w0[j], tsc[j], h);
+        decode_w<F, FOLD>(w0[j], bh[j], bl[j], fs[j]);
       }
     }
 #pragma unroll

@@ -198,12 +198,14 @@ def test_qgemm_mfma_wide_tiles(fmt):
     """Problems with at least 128 tiles of 128x256 (the wide tiling): k a
     multiple of 256 (scales loaded per 256-k trip: one trip, several trips and
     the guarded drain), k not a multiple of 256 (per-step scale loads), ragged
-    m and n, f32 output, and for nvfp4 k not a multiple of 32.  Rows sampled
-    across the 128-row tiles; every column checked."""
+    m and n, f32 output, a ragged last step, and for nvfp4 k not a multiple of
+    32.  Rows sampled across the 128-row tiles; every column checked."""
     cases = [(1000, 4100, 512, torch.bfloat16), (1024, 4096, 256, torch.float32), (1030, 4096, 320, torch.bfloat16),
              (1024, 4096, 2048 + 256, torch.bfloat16)]
     if fmt == "nvfp4":
         cases.append((1024, 4096, 272, torch.bfloat16))
+    if BLOCK[fmt] <= 32:
+        cases.append((1000, 4096, 288, torch.bfloat16))  # ragged last 64-k step (int8: its second block empty)
     rng = np.random.default_rng(77)
     for m, n, k, od in cases:
         if k % BLOCK[fmt]:
