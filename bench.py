@@ -310,17 +310,44 @@ def warm_up(device, seconds=0.5):
         torch.cuda.synchronize(device)
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, budget_s=10.0):
-    """The oracle as it stands (dequant, then fp64 dot) on the host cores."""
+    """The oracle as it stands on the host cores: pack, dequant and the fp64
+    matmul timed separately (the matmul single-threaded and on all threads),
+    then full passes (dequant + all-thread matmul) for ~budget_s seconds."""
     import numpy as np
 
     import oracle
 
     threads = max(1, min(16, os.cpu_count() or 1))
     W, X = __import__("block_scaled_bit_e2m1_amd.workloads", fromlist=["generate"]).generate(wl)
+    t0 = time.perf_counter()
     p = oracle.pack(wl.fmt, W)
+    t_pack = time.perf_counter() - t0
     wb = p["codes"].size + p["scales"].size + (0 if p["biases"] is None else p["biases"].size)
     wb += 4 if wl.fmt == "nvfp4" else 0
+    t0 = time.perf_counter()
+    wd = oracle.dequant_packed(p)
+    t_deq = time.perf_counter() - t0
+    rows = np.arange(max(1, min(wl.m, 16 if wl.op == "qgemv" else 2)))
+    t0 = time.perf_counter()
+    oracle.matmul(X, wd, rows=rows, threads=1)
+    t_mm1 = (time.perf_counter() - t0) / len(rows)
+    t0 = time.perf_counter()
+    oracle.matmul(X, wd, rows=rows, threads=threads)
+    t_mmn = (time.perf_counter() - t0) / len(rows)
+    stages = {"cpu_model": cpu_model(), "nproc": os.cpu_count(), "pack_s": round(t_pack, 4), "dequant_s": round(t_deq, 4),
+              "matmul_s_per_row_1_thread": round(t_mm1, 6), "matmul_s_per_row_all_threads": round(t_mmn, 6)}
     reps, t_total = 0, 0.0
     if wl.op == "qgemv":
         while t_total < budget_s or reps < 2:
@@ -332,7 +359,7 @@ def cpu_baseline(wl, budget_s=10.0):
         v = wb * reps / t_total / 1e9
         return {"value": round(v, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
                 "sample": f"{reps} full passes of {wl.name} (dequant to f32 on 1 core, then fp64 dot on "
-                          f"{threads} threads), {t_total:.1f} s"}
+                          f"{threads} threads), {t_total:.1f} s", **stages}
     rows = max(1, min(wl.m, 16))
     t0 = time.perf_counter()
     wd = oracle.dequant_packed(p)
@@ -340,7 +367,7 @@ def cpu_baseline(wl, budget_s=10.0):
     t = time.perf_counter() - t0
     v = 2.0 * rows * wl.n * wl.k / t / 1e12
     return {"value": round(v, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"dequant + fp64 dot of {rows} of {wl.m} rows of {wl.name}, {t:.1f} s"}
+            "sample": f"dequant + fp64 dot of {rows} of {wl.m} rows of {wl.name}, {t:.1f} s", **stages}
 
 
 def main():
