@@ -55,15 +55,17 @@ constexpr int BK = 64;
 constexpr int LDS_LD = BK + 8;  // bf16 per LDS row: 128 data bytes + 16 pad
 
 template <int F> constexpr bool kSplit = (F == kNVFP8 || F == kINT8_SYM || F == kINT4_AFFINE);
-// int8 in the step-ahead kernel instead: the integer codes go to the MFMA as
-// they are (bf16 holds every q in [-128, 127] exactly), a per-block partial sum
-// P is formed in fp32 and the block's scale is applied to P once, not per
-// element ("fold in that block's scale ONCE", rlx-cpu quant.rs
-// dequant_matmul_int8): acc += s_blk * P_blk.  One MFMA per slice instead of
-// the hi + lo pair.  (int4's bias term would need per-row X sums of every
-// group beside the partial sums; at two waves per SIMD that does not fit in
-// the register file, so int4 keeps hi + lo.)
-template <int F> constexpr bool kFold = (F == kINT8_SYM);
+// int8 / int4 in the step-ahead kernel instead: the integer codes go to the
+// MFMA as they are (bf16 holds every q exactly), a per-block partial sum P is
+// formed in fp32 and the block's scale is applied to P once, not per element
+// ("fold in that block's scale ONCE", rlx-cpu quant.rs dequant_matmul_int8):
+// int8 acc += s_blk * P_blk, one MFMA per slice instead of the hi + lo pair.
+// int4 (value s*q + b, one 64-group per step): acc += s * P after the step,
+// and the bias term b * sum x (the split s*sum q*x + b*sum x of metaltile-std
+// tests/qmm_gpu_correctness.rs cpu_qmm_reference) straight on the MFMA with
+// the group's bias, exact in bf16, broadcast as the B operand: still two
+// MFMAs per slice, but no per-element dequantize and hi/lo split.
+template <int F> constexpr bool kFold = (F == kINT8_SYM || F == kINT4_AFFINE);
 
 __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
   const bf16x2_t v = {(__bf16)a, (__bf16)b};  // round to nearest even
@@ -153,7 +155,7 @@ __device__ __forceinline__ void load_w(WRaw &r, const uint8_t *__restrict__ code
 // one 256-k trip of its column, loaded with one or two wide loads instead of
 // one small load per step.  Needs k % 256 == 0 (every trip whole and its words
 // aligned).  nvfp8 (64 bytes of f32 scales per trip) keeps per-step loads.
-template <int F> constexpr bool kTripSc = F != kNVFP8 && !kFold<F>;
+template <int F> constexpr bool kTripSc = F != kNVFP8 && F != kINT8_SYM;
 template <int F> constexpr int kTripWords =
     (F == kMXFP4 || F == kMXFP8_E4M3 || F == kMXFP8_E5M2) ? 2 : (F == kNVFP4 || F == kINT4_AFFINE) ? 4 : 8;
 
@@ -200,8 +202,9 @@ __device__ __forceinline__ void trip_sc(WRaw &r, const uint32_t (&v)[kTripWords<
 }
 
 // Build the B fragments (hi, and lo for split formats) of the 4 k-slices.
-// FOLD (int8): the integer codes as bf16 (exact) and the step's fold factors
-// fs: the scales of its two 32-blocks.
+// FOLD: the integer codes as bf16 (exact) and the step's fold factors fs:
+// int8 the scales of its two 32-blocks; int4 the group's scale, with lo[0] the
+// group's bias broadcast to all 8 k of the fragment.
 template <int F, bool FOLD = false>
 __device__ __forceinline__ void decode_w(const WRaw &r, bf16x8_t hi[4], bf16x8_t lo[4], float fs[2] = nullptr) {
   const uint32_t cw[8] = {r.c0.x, r.c0.y, r.c0.z, r.c0.w, r.c1.x, r.c1.y, r.c1.z, r.c1.w};
@@ -214,6 +217,20 @@ __device__ __forceinline__ void decode_w(const WRaw &r, bf16x8_t hi[4], bf16x8_t
 #pragma unroll
       for (int i = 0; i < 8; ++i) q[i] = (float)(int)(int8_t)(uint8_t)(cw[2 * t + (i >> 2)] >> (8 * (i & 3)));
       hi[t] = frag(pk_bf16(q[0], q[1]), pk_bf16(q[2], q[3]), pk_bf16(q[4], q[5]), pk_bf16(q[6], q[7]));
+    }
+  } else if constexpr (FOLD && F == kINT4_AFFINE) {
+    fs[0] = bf16_bits_to_f32(r.s0);
+    fs[1] = 0.0f;
+    const uint32_t bb = (r.b0 & 0xFFFFu) * 0x10001u;  // the bias bf16 in both halves
+    lo[0] = frag(bb, bb, bb, bb);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      // even nibbles and odd nibbles as bytes, then bytes to f32 (v_cvt_f32_ubyte, exact) and bf16
+      const uint32_t ev = cw[t] & 0x0F0F0F0Fu, od = (cw[t] >> 4) & 0x0F0F0F0Fu;
+      hi[t] = frag(pk_bf16((float)((ev >> 0) & 0xFFu), (float)((od >> 0) & 0xFFu)),
+                   pk_bf16((float)((ev >> 8) & 0xFFu), (float)((od >> 8) & 0xFFu)),
+                   pk_bf16((float)((ev >> 16) & 0xFFu), (float)((od >> 16) & 0xFFu)),
+                   pk_bf16((float)((ev >> 24) & 0xFFu), (float)((od >> 24) & 0xFFu)));
     }
   } else if constexpr (F == kMXFP4) {
     const float sc = __uint_as_float(r.s0 << 23);  // exponent-only scale operand
@@ -561,6 +578,8 @@ mfma_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
               pacc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bh[j][sl], kZero, 0, 0, 0);
             else
               pacc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bh[j][sl], pacc[i][j], 0, 0, 0);
+            if constexpr (F == kINT4_AFFINE)  // bias * sum of the slice's x
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bl[j][0], acc[i][j], 0, 0, 0);
           }
         if constexpr (last) {
 #pragma unroll
