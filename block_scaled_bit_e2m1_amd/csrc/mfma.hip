@@ -31,9 +31,15 @@
 //                      bits) then bf16; the f32 global scales the accumulator
 //                      once at the end ("global scale multiplied once at the
 //                      end" [rlx-cpu quant.rs, dequant_matmul_nvfp4]);
-//      nvfp8 / int8 / int4: the f32 dequantized value w (one rounding, as the
-//                      standalone dequant) split into bf16 hi + lo, two MFMAs
-//                      per slice; |w - hi - lo| <= 2^-17 |w|.
+//      int8 / int4 (step-ahead schedule): the integer codes, exact in bf16,
+//                      into a per-block partial sum that gets the block scale
+//                      once (int8: slices kept inside one 32-block by a second
+//                      k permutation); int4's bias term b * sum x on the MFMA
+//                      with the bias broadcast as the B operand;
+//      nvfp8 (and int8 / int4 in the small-tile schedule): the f32
+//                      dequantized value w (one rounding, as the standalone
+//                      dequant) split into bf16 hi + lo, two MFMAs per slice;
+//                      |w - hi - lo| <= 2^-17 |w|.
 //  * Workgroup -> tile mapping is XCD-aware: consecutive workgroups are
 //    dispatched round-robin over the 8 XCDs, so tiles are renumbered to give
 //    each XCD a contiguous run of tiles that share X rows (one L2 per XCD).
