@@ -51,10 +51,15 @@ def log(msg):
 
 
 def source_sha(kind):
+    """Hash of the kernel's sources with // comments and blank lines dropped
+    (a comment edit does not change the kernel the counters were taken on)."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[kind]:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
