@@ -130,3 +130,15 @@ def test_rmsnorm_qgemv_validation():
     assert f(bsq.MXFP4, 0, 1, 4, 64, q, q, None, 1.0, q, C.c_void_p(258), 1e-6, bsq.BF16, q, bsq.BF16, None) == bsq.ERR_ALIGN
     assert f(bsq.MXFP4, 16, 1, 4, 64, q, q, None, 1.0, q, q, 1e-6, bsq.BF16, q, bsq.BF16, None) == bsq.ERR_UNSUPPORTED
     assert f(bsq.MXFP4, 0, 0, 4, 64, q, q, None, 1.0, q, q, 1e-6, bsq.BF16, q, bsq.BF16, None) == bsq.OK  # m = 0
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark is one GPU's path: --gpus N > 1 exits with a message, before touching a device."""
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
