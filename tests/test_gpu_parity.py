@@ -206,6 +206,9 @@ def test_qgemm_mfma_wide_tiles(fmt):
         cases.append((1024, 4096, 272, torch.bfloat16))
     if BLOCK[fmt] <= 32:
         cases.append((1000, 4096, 288, torch.bfloat16))  # ragged last 64-k step (int8: its second block empty)
+    # one to three k steps: the step-ahead prologue and guarded drain with nothing in the steady loop
+    kb = 64 if fmt == "int4_affine" else 32
+    cases += [(1024, 4096, kb, torch.bfloat16), (1024, 4096, 3 * kb, torch.float32)]
     rng = np.random.default_rng(77)
     for m, n, k, od in cases:
         if k % BLOCK[fmt]:
