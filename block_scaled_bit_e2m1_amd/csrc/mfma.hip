@@ -64,7 +64,7 @@ template <int F> constexpr bool kSplit = (F == kNVFP8 || F == kINT8_SYM || F == 
 // int8 / int4 in the step-ahead kernel instead: the integer codes go to the
 // MFMA as they are (bf16 holds every q exactly), a per-block partial sum P is
 // formed in fp32 and the block's scale is applied to P once, not per element
-// ("fold in that block's scale ONCE", rlx-cpu quant.rs dequant_matmul_int8):
+// (as rlx-cpu quant.rs dequant_matmul_int8 applies each block scale a single time):
 // int8 acc += s_blk * P_blk, one MFMA per slice instead of the hi + lo pair.
 // int4 (value s*q + b, one 64-group per step): acc += s * P after the step,
 // and the bias term b * sum x (the split s*sum q*x + b*sum x of metaltile-std

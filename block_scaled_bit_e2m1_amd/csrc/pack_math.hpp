@@ -9,11 +9,11 @@
 // lowp_compute_scales and lowp_quantize].
 //
 // Element encoders:
-//   E2M1 by midpoint thresholds ("midpoint-threshold encode"), a tie going to
+//   E2M1 by comparing with the midpoints between levels, a tie going to
 //        the even-mantissa code;
 //   E4M3 / E5M2 / bf16 by integer rounding of the fp64 significand (nearest,
-//        ties to even), saturating E4M3 at 448 ("+-448 saturation, no inf")
-//        and E5M2 at 57344 ("e5m2_encode now saturates finite inputs")
+//        ties to even), saturating E4M3 at +-448 (the format has no inf)
+//        and finite E5M2 inputs at +-57344
 //   [metaltile PR #250, codec commits].
 // Quotients w / S are formed in fp64, which decides every rounding exactly
 // for these operand widths.

@@ -14,8 +14,8 @@
 // carry no bounds checks, so no wait separates them.  Per 8-element sub-chunk
 // the
 // unscaled element values are dotted with X in fp32; the block scale is folded
-// once per block ("fold in that block's scale ONCE (not per element)" [rlx-cpu
-// quant.rs, dequant_matmul_int8]) and the nvfp4 global once at the end
+// once per block, not per element [rlx-cpu quant.rs, dequant_matmul_int8,
+// which applies each block's scale a single time] and the nvfp4 global once at the end
 // [rlx-cpu quant.rs, dequant_matmul_nvfp4].  int4 affine folds s and b per
 // group as s * sum(q*x) + b * sum(x) [metaltile-std tests/qmm_gpu_correctness.rs,
 // cpu_qmm_reference].  The wave's partial sums are reduced with DPP row

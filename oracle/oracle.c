@@ -18,7 +18,7 @@
  *            kernel"; rlx-cpu quant.rs, lowp_dequantize].
  *   matmul   ref[i,j] = sum_p X[i,p] * Wd[j,p] in fp64, with
  *            den[i,j] = sum_p |X[i,p] * Wd[j,p]| alongside (the
- *            "dequant-then-dot" oracle of PR #250's qgemv / qmm commits).
+ *            dequantize-then-dot reference of PR #250's qgemv / qmm commits).
  *   rmsnorm  Xhat[i,p] = X[i,p] * g[p] / sqrt(mean_p X[i,p]^2 + eps), the
  *            activation of the fused RMSNorm + dequantizing GEMV [PR #250,
  *            commit adding the block-scaled fused RMSNorm + GEMV].
@@ -181,7 +181,7 @@ double orc_bf16_value(uint16_t bits)
 /* Format table.                                                             */
 /* ------------------------------------------------------------------------ */
 
-/* Block sizes along k: 32 for the MX formats [PR #250 "E8M0 pow-2 | 32"],
+/* Block sizes along k: 32 for the MX formats [PR #250 format table],
  * 16 for nvfp4/nvfp8, 64 for int4 affine groups [metaltile-std
  * qmm_gpu_correctness.rs, group_size 64], 32 for int8 blocks. */
 int orc_block(int fmt)
@@ -291,7 +291,7 @@ static double decode_elem(int fmt, unsigned c)
  *          (symmetric, +-127 [PR #250, int8 codec commit]).
  *   int4:  per 64-group s = bf16((max-min)/15), b = bf16(min),
  *          q = clamp(rne((w-b)/s), 0, 15); value s*q + b [qmm_gpu_correctness.rs,
- *          cpu_qmm_reference; "quantized per group by min/max"].
+ *          cpu_qmm_reference; groups quantized by their min and max].
  * Every code is chosen against the scale exactly as stored; a zero effective
  * scale gives code 0 (rlx-cpu quant.rs, lowp_quantize).  Quotients are formed
  * in fp64.  Non-finite input is rejected. */
