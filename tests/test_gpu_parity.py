@@ -544,6 +544,15 @@ def test_rmsnorm_qgemv_parity(fmt):
         check_bound(out, ref, den, tol, f"rmsnorm_qgemv {fmt} m={m} n={n} k={k} {act}", act == "bf16")
 
 
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp8_e4m3", "int4_affine"])
+def test_rmsnorm_qgemv_lds_limit(fmt):
+    """One bf16 row: x*g is staged in LDS up to k = 8192; k = 8192 takes that
+    path and k = 8256 the per-wave one.  Both against the oracle."""
+    for k in (8192, 8256):
+        out, ref, den = _rmsnorm_case(fmt, 1, 200, k, "bf16", 1e-6, seed=k)
+        check_bound(out, ref, den, 2e-3, f"rmsnorm_qgemv {fmt} m=1 k={k}", True)
+
+
 def test_rmsnorm_qgemv_decode_shape_full():
     """The decode shape (nvfp4, n = k = 4096, bf16) at full size against the
     full oracle, and the f32 output of the same launch."""
