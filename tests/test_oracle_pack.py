@@ -195,6 +195,41 @@ def test_int8_amax_rule(orc):
     assert (np.abs(q).max(-1) == 127).all()
 
 
+def test_nvfp8_amax_rule(orc):
+    """nvfp8 keeps one f32 scale per 16-block chosen so the block amax lands on
+    E4M3's largest finite value, 448 (format table of metaltile PR #250: nvfp8 is
+    E4M3 elements, block 16, FP32 scale; rlx-cpu quant.rs lowp_compute_scales
+    divides the amax by the element format's largest finite value).  Pinned
+    without the oracle's formula: the top element of every non-zero block must
+    take code 0x7E (448 from torch's float8_e4m3fn table, which a 240 maximum
+    would miss: its top code would be 0x77) and must reconstruct the amax to
+    within f32 rounding (which a 480 maximum would miss: that saturates the top
+    element 6.7% low).  The stored scale is also the correctly rounded f32
+    quotient, and zero blocks keep scale 1 and all-zero codes."""
+    rng = np.random.default_rng(24)
+    w = (rng.standard_normal((24, 256)) * 0.02).astype(np.float32)
+    w[3, 16:32] = 0.0                                   # a zero block
+    w[5, :16] *= 1e-30                                  # a block near the bottom of f32
+    w[7, 32:48] *= 1e30                                 # a block near the top
+    p = orc.pack("nvfp8", w)
+    s = p["scales"].view(np.float32).reshape(24, -1).astype(np.float64)
+    codes = codes_of("nvfp8", p).reshape(24, -1, 16)
+    t = torch_e4m3_table()
+    blocks = w.astype(np.float64).reshape(24, -1, 16)
+    amax = np.abs(blocks).max(-1)
+    nz = amax > 0
+    top = np.abs(blocks).argmax(-1)
+    top_code = np.take_along_axis(codes, top[..., None], -1)[..., 0]
+    assert ((top_code[nz] & 0x7F) == 0x7E).all(), np.argwhere(nz & ((top_code & 0x7F) != 0x7E))[:5]
+    assert t[0x7E] == 448.0
+    recon = t[top_code] * s
+    top_val = np.take_along_axis(blocks, top[..., None], -1)[..., 0]
+    assert (np.abs(recon[nz] - top_val[nz]) <= 2.0 ** -22 * amax[nz]).all()
+    want = (amax.astype(np.float32) / np.float32(448.0)).astype(np.float64)
+    assert (s[nz] == want[nz]).all()
+    assert (s[~nz] == 1.0).all() and (codes[~nz] == 0).all()
+
+
 def test_nonfinite_rejected(orc):
     w = np.zeros((2, 32), dtype=np.float32)
     w[1, 3] = np.nan
