@@ -58,6 +58,12 @@ hipError_t launch_rows_norm(const QWeight &w, int64_t m, const void *x, int xt, 
 // row and sets *status (may be null) to 1.
 hipError_t launch_rows_gather(const QWeight &w, int64_t m, const void *x, int xt, const int32_t *eids, int64_t nexp,
                               int *status, void *out, int ot, hipStream_t s);
+// Decode GEMV kernel (gemv.hip): bf16 activation rows that each stream the
+// weight once (m == 1, or every routed row when routed), whole 16-byte code
+// chunks (k % 32 == 0 for 4-bit codes, k % 16 == 0 for 8-bit).
+bool gemv_applies(const QWeight &w, int64_t m, int xt, bool routed);
+hipError_t launch_gemv(const QWeight &w, int64_t m, const void *x, void *out, int ot, const int32_t *eids,
+                       int64_t nexp, int *status, hipStream_t s);
 // MFMA kernel: bf16 X, any m >= 1.
 hipError_t launch_mfma(const QWeight &w, int64_t m, const void *x, void *out, int ot, hipStream_t s);
 // Zero-fill an output of `bytes` bytes (k == 0 case).

@@ -1,0 +1,495 @@
+// gemv.hip -- decode GEMV for bf16 activation rows that each stream the
+// weight once: out[i,j] = sum_p x[i,p] * dequant(W)[j,p] for m = 1 (the
+// decode step) and for every routed row of the expert gather.
+//
+// The weight stream is the whole cost of this step [rlx-cpu quant.rs,
+// dequant_matmul_int8: memory bandwidth, not flops, since the weights dominate;
+// metaltile PR #250, qgemv bench commit: the one-row-per-threadgroup kernels
+// read latency-bound at low bandwidth].  Two measured facts about MI355X
+// shape the design:
+//  * A wave's 16-byte row loads spread over many HBM channels, so when every
+//    wave issues all its loads at once each wave's data completes near the
+//    end of the stream; the decode arithmetic (one VALU instruction per
+//    element: v_cvt_scalef32_pk_bf16_* + v_dot2_f32_bf16, both full rate)
+//    then runs after the data, not beside it.  Giving each wave several
+//    row groups whose loads are consumed in issue order lets the first
+//    groups' arithmetic overlap the rest of the stream.
+//  * Per-row wave reductions cost about as much as the dot products at this
+//    size, so the R rows of a group are reduced jointly: gfx950's
+//    v_permlane32_swap / v_permlane16_swap fold 2 or 4 rows' partial sums
+//    into halves / quarters of the wave, then 4 DPP steps finish all rows.
+//
+// Geometry: a workgroup of WPG waves; KW consecutive waves split the k
+// chunks of a row group (lane l of wave ks takes the 16-byte chunk
+// 64*(KW*round + ks) + l, i.e. 32 elements of 4-bit or 16 of 8-bit codes)
+// and combine through LDS; each row group has S sequential groups of R rows.
+// Loads are issued in the order the arithmetic consumes them, the first row
+// group's codes ahead of everything else (x, the chunk's activations shared by
+// all rows, follows them).  The block
+// scale is folded once per block [rlx-cpu quant.rs, dequant_matmul_int8
+// applies each block scale a single time], the nvfp4 global once at the end
+// [rlx-cpu quant.rs, dequant_matmul_nvfp4], int4 as s*sum(q*x) + b*sum(x)
+// [metaltile-std tests/qmm_gpu_correctness.rs, cpu_qmm_reference].
+//
+// Expert routing (eids != null): activation row i multiplies expert eids[i]
+// of a stacked [E*n, k] weight [metaltile PR #250, commit adding the
+// per-token expert-routed qmm]; an id outside [0, E) loads nothing, leaves
+// that output row zero and sets *status to 1.
+#include "bsq_internal.hpp"
+#include "codec.hpp"
+#include "dot.hpp"
+
+#include <type_traits>
+
+namespace bsq {
+namespace {
+
+using namespace dot;
+
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+// Sum over each row of 16 lanes (every lane of the row receives it).
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));  // half-row mirror
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));  // row mirror
+  return v;
+}
+
+// v_permlane32_swap: lanes 32..63 of a trade places with lanes 0..31 of b.
+// Returns the sums lo + hi of the swapped pair: lanes 0..31 then hold
+// a[l] + a[l+32], lanes 32..63 hold b[l-32] + b[l].
+__device__ __forceinline__ float fold32(float a, float b) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+// v_permlane16_swap: the same within each half, between 16-lane rows.
+// Lanes 0..15 then hold a[l] + a[l+16], lanes 16..31 b[l-16] + b[l], and
+// likewise for lanes 32..63.
+__device__ __forceinline__ float fold16(float a, float b) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// Joint wave reduction of R per-lane partial sums (R = 1, 2 or 4): row r's
+// total lands in lane out_lane<R>(r).
+template <int R>
+__device__ __forceinline__ float joint_sum(const float (&a)[R]) {
+  static_assert(R == 1 || R == 2 || R == 4, "joint reduction of 1, 2 or 4 rows");
+  if constexpr (R == 1) {
+    return wave_sum(a[0]);
+  } else if constexpr (R == 2) {
+    const float t = fold32(a[0], a[1]);  // lanes 0-31 row 0, 32-63 row 1
+    return row16_sum(fold16(t, t));      // each 16-lane row: its half's total
+  } else {
+    const float s0 = fold32(a[0], a[2]);  // lanes 0-31 row 0, 32-63 row 2
+    const float s1 = fold32(a[1], a[3]);  // lanes 0-31 row 1, 32-63 row 3
+    return row16_sum(fold16(s0, s1));     // lanes 16r..16r+15: row r
+  }
+}
+template <int R> __device__ __forceinline__ int out_lane(int r) { return R == 1 ? 0 : (R == 2 ? 32 * r : 16 * r); }
+
+template <int F> constexpr int kE = Traits<F>::kBits == 4 ? 32 : 16;  // elements per 16-byte chunk
+// chunks per stored scale word (nvfp4: one 16-bit pair of micro-scales per chunk)
+template <int F> constexpr int kCPS = F == kNVFP4 ? 1 : (Traits<F>::kBlock > kE<F> ? Traits<F>::kBlock / kE<F> : 1);
+
+// Raw scale (and int4 bias) of chunk ch of a row whose scales start at srow
+// (bytes) and biases at brow.
+template <int F>
+__device__ __forceinline__ void load_sc(const uint8_t *__restrict__ srow, const uint16_t *__restrict__ brow,
+                                        uint32_t ch, uint32_t &s, uint32_t &b) {
+  if constexpr (F == kNVFP4) {
+    s = *reinterpret_cast<const uint16_t *>(srow + 2 * ch);
+  } else {
+    const uint32_t bi = ch / kCPS<F>;
+    s = load_scale_raw<F>(srow, bi);
+    if constexpr (F == kINT4_AFFINE) b = brow[bi];
+  }
+}
+
+// The block scale as f32.  E8M0: the hardware fp8 conversion of 1.0 with the
+// byte as its exponent-only scale operand is exactly 2^(b-127), byte 0 giving
+// the f32 subnormal 2^-127 and byte 255 NaN, with no compare.
+template <int F>
+__device__ __forceinline__ float block_scale(uint32_t s) {
+  if constexpr (F == kMXFP4 || F == kMXFP8_E4M3 || F == kMXFP8_E5M2) {
+    const f32x2_t v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(0x38u, __uint_as_float((s & 0xFFu) << 23), false);
+    return v[0];
+  } else {
+    return scale_value<F>(s);
+  }
+}
+
+// acc + this chunk's contribution, its block scale(s) folded once.
+template <int F>
+__device__ __forceinline__ float chunk_dot(v4u c, uint32_t s, uint32_t b, const uint4 (&xq)[kE<F> / 8], float acc) {
+  if constexpr (F == kNVFP4) {
+    float p0 = dot8_bf16<F>(c.x, 0u, xq[0], 0.0f);
+    p0 = dot8_bf16<F>(c.y, 0u, xq[1], p0);
+    float p1 = dot8_bf16<F>(c.z, 0u, xq[2], 0.0f);
+    p1 = dot8_bf16<F>(c.w, 0u, xq[3], p1);
+    // both E4M3 micro-scales in one conversion (OCP E4M3: exact, 0x7F is NaN)
+    const f32x2_t sv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(s, 1.0f, false);
+    acc = __builtin_fmaf(p0, sv[0], acc);
+    return __builtin_fmaf(p1, sv[1], acc);
+  } else if constexpr (Traits<F>::kBits == 4) {  // mxfp4, int4: one scale (group) per chunk
+    float p = dot8_bf16<F>(c.x, 0u, xq[0], 0.0f);
+    p = dot8_bf16<F>(c.y, 0u, xq[1], p);
+    p = dot8_bf16<F>(c.z, 0u, xq[2], p);
+    p = dot8_bf16<F>(c.w, 0u, xq[3], p);
+    acc = __builtin_fmaf(p, block_scale<F>(s), acc);
+    if constexpr (F == kINT4_AFFINE) {
+      float xs = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t v[4] = {xq[q].x, xq[q].y, xq[q].z, xq[q].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xs += __uint_as_float(v[i] << 16) + __uint_as_float(v[i] & 0xFFFF0000u);
+      }
+      acc = __builtin_fmaf(xs, bf16_bits_to_f32(b), acc);
+    }
+    return acc;
+  } else {  // 8-bit codes: 16 elements, one scale
+    float p = dot8_bf16<F>(c.x, c.y, xq[0], 0.0f);
+    p = dot8_bf16<F>(c.z, c.w, xq[1], p);
+    return __builtin_fmaf(p, block_scale<F>(s), acc);
+  }
+}
+
+// Launch parameters, with the per-row byte counts and the chunk count worked
+// out on the host (the kernel does no division by a runtime value).
+struct GemvParams {
+  const uint8_t *codes;
+  const uint8_t *scales;
+  const uint16_t *biases;
+  const uint16_t *x;
+  void *out;
+  const int32_t *eids;
+  int *status;
+  int64_t n, k, nexp;  // output rows, reduction length, experts in the stack
+  uint64_t rowb;       // code bytes per weight row
+  uint64_t srowb;      // scale bytes per weight row
+  float global;
+  int ot;              // 0: f32 out, 1: bf16 out
+  int C;               // 16-byte code chunks per row
+};
+
+// O32: every code and scale byte offset of the (stacked) weight fits in 31
+// bits, so all index arithmetic is unsigned 32-bit and rows are addressed as
+// a 32-bit offset from the weight's base (global_load with a scalar base and
+// a vector offset).  The per-wave set-up before the first load is what every
+// wave of a CU waits behind on the shared scalar unit: with 64-bit row
+// pointers and signed 64-bit divisions it was ~160 scalar instructions per
+// wave (nvfp4 4096 x 4096: 4.06 us).
+// ONE: every wave has exactly one full round (k = 64 * KW chunks), so the
+// round loop, its guards and their scalar set-up drop out.
+template <int F, int KW, int R, int S, int WPG, bool O32, bool ONE>
+__global__ void __launch_bounds__(WPG * 64) gemv_kernel(const GemvParams p) {
+  constexpr int E = kE<F>, XQ = E / 8, RG = WPG / KW, RS = R * S;
+  constexpr int SB = (F == kNVFP8 || F == kINT8_SYM) ? 4 : (F == kINT4_AFFINE ? 2 : 1);  // bytes per scale
+  typedef typename std::conditional<O32, uint32_t, uint64_t>::type idx_t;
+  static_assert(WPG % KW == 0 && (KW & (KW - 1)) == 0, "k split: a power of two dividing the waves");
+  const int lane = threadIdx.x & 63;
+  const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index: uniform
+  const uint32_t rg = w / KW, ks = w % KW;
+  // Set-up kept short and in 32-bit unsigned arithmetic on the O32 path: it
+  // runs on the CU's shared scalar unit for every wave before its first load.
+  const idx_t n = (idx_t)p.n;
+  const idx_t rowb = (idx_t)p.rowb, srowb = (idx_t)p.srowb;
+  const uint32_t C = (uint32_t)p.C;
+  const uint32_t i = blockIdx.y;  // activation row
+  const idx_t jb = ((idx_t)blockIdx.x * RG + rg) * RS;
+  idx_t jbase = 0;
+  bool skip = false;
+  if (p.eids) {
+    const int64_t e = p.eids[i];
+    skip = e < 0 || e >= p.nexp;
+    if (skip && p.status && blockIdx.x == 0 && threadIdx.x == 0) *p.status = 1;
+    jbase = skip ? 0 : (idx_t)e * n;
+  }
+  const uint16_t *xr = p.x + (idx_t)i * (idx_t)p.k;
+  __shared__ float red[KW > 1 ? WPG : 1][RS];
+
+  float acc[S][R];
+  idx_t coff[S][R], soff[S][R];  // byte offsets of each row's codes and scales
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      acc[s][r] = 0.0f;
+      // rows past n read row n-1 and are never stored
+      const idx_t jr = jbase + __builtin_elementwise_min(jb + (idx_t)(s * R + r), n - 1);
+      coff[s][r] = jr * rowb;
+      soff[s][r] = jr * srowb;
+    }
+
+  // One round: lane l of this wave takes chunk base + l of every row of the
+  // group.  Full rounds carry no bounds checks; the last (guarded) round of a
+  // wave masks chunks past the row.
+  auto store = [&](idx_t j, float v) {
+    if constexpr (F == kNVFP4) v *= p.global;
+    const uint64_t o = (uint64_t)i * (uint64_t)n + j;
+    if (p.ot == 0) reinterpret_cast<float *>(p.out)[o] = v;
+    else reinterpret_cast<uint16_t *>(p.out)[o] = f32_to_bf16_bits(v);
+  };
+  // Group s is complete: reduce its R rows jointly and store them (KW == 1)
+  // or leave them in LDS for the k-split combine.
+  auto finish = [&](int s) {
+    const float v = joint_sum<R>(acc[s]);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (lane == out_lane<R>(r)) {
+        if constexpr (KW == 1) {
+          if (jb + s * R + r < n) store(jb + s * R + r, v);
+        } else {
+          red[w][s * R + r] = v;
+        }
+      }
+    }
+  };
+
+  auto round = [&](auto guard, auto last, uint32_t base) {
+    constexpr bool kG = decltype(guard)::value;
+    constexpr bool kLast = decltype(last)::value;
+    const uint32_t ch = base + lane;
+    const bool in = !kG || ch < C;
+    const uint32_t cc = in ? ch : 0u;
+    uint4 xq[XQ];
+    v4u cw[S][R];
+    uint32_t sw[S][R], bw[S][R];
+    auto load_group = [&](int s) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        cw[s][r] = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p.codes + (coff[s][r] + (idx_t)cc * 16)));
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        bw[s][r] = 0u;
+        load_sc<F>(p.scales + soff[s][r], p.biases + soff[s][r] / SB, cc, sw[s][r], bw[s][r]);
+      }
+    };
+    // Issue order (fenced): the first group's codes and scales, then x, then
+    // the later groups.  The HBM requests leave first; x (an L2 hit) must not
+    // hold them back in the address unit, and it still arrives before the
+    // first group is consumed, so the in-order wait for that group covers it.
+    load_group(0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < XQ; ++q) xq[q] = reinterpret_cast<const uint4 *>(xr + (idx_t)cc * E)[q];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 1; s < S; ++s) load_group(s);
+    // every load of the round is in flight before the first use
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      if (in) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          // An empty asm that reads and writes the loaded words pins their
+          // first use here: otherwise instruction selection may place the
+          // scale decode right after its load, and the wait it needs would
+          // hold back the loads issued after it.
+          asm volatile("" : "+v"(cw[s][r]), "+v"(sw[s][r]));
+          acc[s][r] = chunk_dot<F>(cw[s][r], sw[s][r], bw[s][r], xq, acc[s][r]);
+        }
+      }
+      // in the wave's last round a group's sums are final as soon as its dots
+      // are: its reduction overlaps the arrival of the later groups' data
+      if constexpr (kLast) finish(s);
+    }
+  };
+  // rounds whose 64 chunks all lie inside the row, then at most one partial;
+  // the wave's last round finishes each group as it goes
+  constexpr uint32_t step = 64 * KW;
+  const uint32_t first = ks * 64;
+  constexpr std::integral_constant<bool, false> kNo{};
+  constexpr std::integral_constant<bool, true> kYes{};
+  if constexpr (ONE) {
+    if (!skip) {
+      round(kNo, kYes, first);
+    } else {
+#pragma unroll
+      for (int s = 0; s < S; ++s) finish(s);
+    }
+  } else {
+  const uint32_t nfull = skip ? 0u : (C >= first + 64 ? (C - first - 64) / step + 1 : 0u);
+  const bool partial = !skip && first + nfull * step < C;
+  if (partial) {
+    for (uint32_t rr = 0; rr < nfull; ++rr) round(kNo, kNo, first + rr * step);
+    round(kYes, kYes, first + nfull * step);
+  } else if (nfull > 0) {
+    for (uint32_t rr = 0; rr + 1 < nfull; ++rr) round(kNo, kNo, first + rr * step);
+    round(kNo, kYes, first + (nfull - 1) * step);
+  } else {
+    // no chunk for this wave (a bad expert id, or k shorter than the split)
+#pragma unroll
+    for (int s = 0; s < S; ++s) finish(s);
+  }
+  }
+  if constexpr (KW > 1) {
+    __syncthreads();
+    if (ks == 0 && lane < RS && jb + lane < n) {
+      float t = 0.0f;
+#pragma unroll
+      for (int q = 0; q < KW; ++q) t += red[rg * KW + q][lane];
+      store(jb + lane, t);
+    }
+  }
+}
+
+// One-round kernel: every wave covers its k split in a single round (the row
+// is exactly 64 * KW chunks: k = 4096 for both code widths).  Written with
+// plain per-lane 32-bit index arithmetic and 64-bit lane pointers; measured
+// faster than the general kernel with its single round selected at compile
+// time (nvfp4 4096 x 4096: 3.65 vs 3.9 us; the set-up of the general kernel,
+// scalar row offsets and scalar-base loads, costs the difference).
+template <int F, int KW, int R, int S, int WPG>
+__global__ void __launch_bounds__(WPG * 64) gemv1_kernel(const GemvParams p) {
+  constexpr int E = kE<F>, XQ = E / 8, RG = WPG / KW, RS = R * S;
+  constexpr int SB = (F == kNVFP8 || F == kINT8_SYM) ? 4 : (F == kINT4_AFFINE ? 2 : 1);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int rg = w / KW, ks = w - rg * KW;
+  const int n = (int)p.n;
+  const int rowb = (int)p.rowb, srowb = (int)p.srowb;
+  const int i = blockIdx.y;
+  const int j0 = (blockIdx.x * RG + rg) * RS;
+  const int ch = ks * 64 + lane;
+  int jbase = 0;
+  bool skip = false;
+  if (p.eids) {
+    const int e = p.eids[i];
+    skip = e < 0 || (int64_t)e >= p.nexp;
+    if (skip && p.status && blockIdx.x == 0 && threadIdx.x == 0) *p.status = 1;
+    jbase = skip ? 0 : e * n;
+  }
+  __shared__ float red[KW > 1 ? WPG : 1][RS];
+  v4u cw[S][R];
+  uint32_t sw[S][R], bw[S][R];
+  uint4 xq[XQ];
+  float acc[S][R];
+  auto load_group = [&](int s) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int jr = jbase + min(j0 + s * R + r, n - 1);  // rows past n: read row n-1, never stored
+      bw[s][r] = 0u;
+      load_sc<F>(p.scales + (size_t)jr * srowb, p.biases + (size_t)jr * (srowb / SB), (uint32_t)ch, sw[s][r], bw[s][r]);
+      cw[s][r] = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p.codes + (size_t)jr * rowb) + ch);
+    }
+  };
+  if (!skip) {
+    load_group(0);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint16_t *xr = p.x + (size_t)i * (size_t)p.k;
+#pragma unroll
+    for (int q = 0; q < XQ; ++q) xq[q] = reinterpret_cast<const uint4 *>(xr + ch * E)[q];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 1; s < S; ++s) load_group(s);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  auto store = [&](int j, float v) {
+    if constexpr (F == kNVFP4) v *= p.global;
+    const size_t o = (size_t)i * (size_t)n + j;
+    if (p.ot == 0) reinterpret_cast<float *>(p.out)[o] = v;
+    else reinterpret_cast<uint16_t *>(p.out)[o] = f32_to_bf16_bits(v);
+  };
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      acc[s][r] = 0.0f;
+      if (!skip) {
+        asm volatile("" : "+v"(cw[s][r]), "+v"(sw[s][r]));
+        acc[s][r] = chunk_dot<F>(cw[s][r], sw[s][r], bw[s][r], xq, 0.0f);
+      }
+    }
+    const float v = joint_sum<R>(acc[s]);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (lane == out_lane<R>(r)) {
+        if constexpr (KW == 1) {
+          if (j0 + s * R + r < n) store(j0 + s * R + r, v);
+        } else {
+          red[w][s * R + r] = v;
+        }
+      }
+    }
+  }
+  if constexpr (KW > 1) {
+    __syncthreads();
+    if (ks == 0 && lane < RS && j0 + lane < n) {
+      float t = 0.0f;
+#pragma unroll
+      for (int q = 0; q < KW; ++q) t += red[rg * KW + q][lane];
+      store(j0 + lane, t);
+    }
+  }
+}
+
+// Measured on MI355X (graph replay, cold weights): 4-bit codes take KW = 2,
+// two sequential groups of 2 rows, 8-wave workgroups (nvfp4 4096 x 4096:
+// 3.62 us per launch; one group of 2 rows: 3.82; the one-wave-per-row-pair
+// kernel: 4.76); 8-bit codes take KW = 4, one group of 2 rows, 4 waves
+// (mxfp8 14336 x 4096: 10.7 us against a 10.1 us pure read of the codes).
+template <int F>
+hipError_t run(const QWeight &w, int64_t m, const void *x, void *out, int ot, const int32_t *eids, int64_t nexp,
+               int *status, hipStream_t s) {
+  constexpr bool k4 = Traits<F>::kBits == 4;
+  constexpr int KW = k4 ? 2 : 4, R = 2, S = k4 ? 2 : 1, WPG = k4 ? 8 : 4;
+  constexpr int rows_per_wg = (WPG / KW) * R * S;
+  const int64_t wgs = (w.n + rows_per_wg - 1) / rows_per_wg;
+  if (wgs > 0x7FFFFFFF || m > 65535) return hipErrorInvalidValue;
+  // every byte offset of the (stacked) weight in 31 bits: 32-bit index math
+  GemvParams p;
+  p.codes = (const uint8_t *)w.codes;
+  p.scales = (const uint8_t *)w.scales;
+  p.biases = (const uint16_t *)w.biases;
+  p.x = (const uint16_t *)x;
+  p.out = out;
+  p.eids = eids;
+  p.status = status;
+  p.n = w.n;
+  p.k = w.k;
+  p.nexp = nexp;
+  p.rowb = (uint64_t)(k4 ? w.k / 2 : w.k);
+  constexpr int SB = (F == kNVFP8 || F == kINT8_SYM) ? 4 : (F == kINT4_AFFINE ? 2 : 1);
+  p.srowb = (uint64_t)(w.k / Traits<F>::kBlock) * SB;
+  p.global = w.global;
+  p.ot = ot;
+  p.C = (int)(w.k / (k4 ? 32 : 16));
+  const int64_t total_rows = w.n * (eids ? nexp : 1);
+  // 32-bit offsets: the codes (scales are smaller) and the activation rows
+  const bool o32 = total_rows * (int64_t)p.rowb < ((int64_t)1 << 31) && m * w.k < ((int64_t)1 << 30);
+  const bool one = p.C == 64 * KW;
+  const dim3 grid((unsigned)wgs, (unsigned)m), block(WPG * 64);
+  if (o32 && one) hipLaunchKernelGGL((gemv1_kernel<F, KW, R, S, WPG>), grid, block, 0, s, p);
+  else if (o32) hipLaunchKernelGGL((gemv_kernel<F, KW, R, S, WPG, true, false>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((gemv_kernel<F, KW, R, S, WPG, false, false>), grid, block, 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool gemv_applies(const QWeight &w, int64_t m, int xt, bool routed) {
+  // bf16 activations, whole 16-byte code chunks, one weight pass per row
+  const int64_t E = is_4bit(w.fmt) ? 32 : 16;
+  return xt == 1 && w.k % E == 0 && w.k / E < ((int64_t)1 << 30) && (m == 1 || routed);
+}
+
+hipError_t launch_gemv(const QWeight &w, int64_t m, const void *x, void *out, int ot, const int32_t *eids,
+                       int64_t nexp, int *status, hipStream_t s) {
+  switch (w.fmt) {
+    case kMXFP4: return run<kMXFP4>(w, m, x, out, ot, eids, nexp, status, s);
+    case kNVFP4: return run<kNVFP4>(w, m, x, out, ot, eids, nexp, status, s);
+    case kMXFP8_E4M3: return run<kMXFP8_E4M3>(w, m, x, out, ot, eids, nexp, status, s);
+    case kMXFP8_E5M2: return run<kMXFP8_E5M2>(w, m, x, out, ot, eids, nexp, status, s);
+    case kNVFP8: return run<kNVFP8>(w, m, x, out, ot, eids, nexp, status, s);
+    case kINT4_AFFINE: return run<kINT4_AFFINE>(w, m, x, out, ot, eids, nexp, status, s);
+    case kINT8_SYM: return run<kINT8_SYM>(w, m, x, out, ot, eids, nexp, status, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace bsq
