@@ -6,11 +6,14 @@ stream, decode, block-scale fold and dot, A1-A4 of the hot path):
     E4M3 micro-scales per 16 + f32 global, x bf16 ~ N(0,1), out bf16.
 
 `value` is the weight-stream rate (codes + scales + global bytes per launch
-divided by the time per launch) with every input already resident in HBM.
-Launches rotate over enough distinct copies of the packed weight (> 512 MB)
-that each launch reads its weight from HBM, not from the 256 MB Infinity
-Cache; launches are replayed from a HIP graph so host launch cost is not
-measured.  The same line carries the prefill GEMM (mxfp4, m=2048, n=k=4096)
+divided by the host-clock time per launch over exactly --steps launches)
+with every input already resident in HBM.  Launches rotate over distinct
+copies of the packed weight (640 MB in all) and 640 MB of other memory is
+read and written just before the timed region, so every timed launch reads
+its weight from HBM, not from the 256 MB Infinity Cache; launches are
+replayed from HIP graphs captured before the clock starts.  The calibration
+kernels give the measured ceilings (cold streaming read of the same bytes;
+register-only bf16 MFMA loop) reported beside the vendor peaks.  The same line carries the prefill GEMM (mxfp4, m=2048, n=k=4096)
 and the other decode/prefill workloads as `extra` entries, a `roofline` object
 for the timed kernel, and the CPU oracle timed on a bounded sample as
 `cpu_baseline`.
@@ -35,10 +38,14 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
 MFMA_FP8_PEAK_TFLOPS = 5000.0   # dense fp8 (an fp8 operand on either side of the scaled MFMA)
 MFMA_FP4_PEAK_TFLOPS = 10100.0  # dense fp4 (both operands fp4)
 ROTATE_BYTES = 640 << 20        # distinct weight copies per rotation (> 2x the 256 MB MALL)
+MALL_BYTES = 256 << 20          # MI355X Infinity Cache
+FLUSH_BYTES = 640 << 20         # read + written before every timed region, evicting the MALL and L2s
+STEADY_STEPS = 2000             # launches of the region that gives the roofline's launch duration
 
 # sources each timed kernel is compiled from: traffic counters taken on an
 # older version of any of them are not reported
-KERNEL_SOURCES = {"qgemv": ["block_scaled_bit_e2m1_amd/csrc/rows.hip", "block_scaled_bit_e2m1_amd/csrc/codec.hpp"],
+KERNEL_SOURCES = {"qgemv": ["block_scaled_bit_e2m1_amd/csrc/gemv.hip", "block_scaled_bit_e2m1_amd/csrc/dot.hpp",
+                            "block_scaled_bit_e2m1_amd/csrc/codec.hpp"],
                   "qgemm": ["block_scaled_bit_e2m1_amd/csrc/mfma.hip", "block_scaled_bit_e2m1_amd/csrc/codec.hpp",
                             "block_scaled_bit_e2m1_amd/csrc/epilogue.hpp"],
                   "qgemm_mx": ["block_scaled_bit_e2m1_amd/csrc/mxmma.hip", "block_scaled_bit_e2m1_amd/csrc/codec.hpp",
@@ -110,50 +117,141 @@ def launch(wl, d, i):
         bsq.qgemm(w, d["x"], out=d["out"])
 
 
-def time_workload(wl, steps, warmup, device, rotate=True, per_graph=None):
-    """Per-launch time (ms) over `steps` launches replayed from HIP graphs,
-    measured with events on the launch stream and with the host clock."""
+_FLUSH = None
+
+
+def flush_caches(device, stream):
+    """Read and write FLUSH_BYTES of unrelated memory on the launch stream, so
+    no weight copy is left in the 256 MB Infinity Cache or the L2s."""
     import torch
 
-    d = setup(wl, device, rotate)
-    if per_graph is None:
-        per_graph = d["copies"] if wl.op == "qgemv" else (4 if wl.m > 8 else 64)
-    per_graph = max(1, min(per_graph, steps))
+    global _FLUSH
+    if _FLUSH is None:
+        _FLUSH = torch.zeros(FLUSH_BYTES // 4, dtype=torch.int32, device=device)
+    with torch.cuda.stream(stream):
+        _FLUSH.add_(1)
+
+
+def timed_calls(launch, n_items, steps, warmup, device, flush=True):
+    """Time exactly `steps` calls of launch(i), i cycling over n_items distinct
+    inputs.  The calls are replayed from HIP graphs captured before the clock
+    starts: one graph of per = min(steps, max(n_items, 64)) calls replayed
+    steps // per times, and one of the remaining calls.  W eager calls warm
+    up first and the whole timed sequence (replays, flush, synchronize) is
+    rehearsed twice untimed; then (flush=True) the caches are flushed, so
+    the first pass over the inputs reads HBM, and later passes do too when the
+    n_items inputs exceed the MALL.  Returns (event ms per call on the launch
+    stream, host-clock ms per call), both over the whole timed region."""
+    import torch
+
     stream = torch.cuda.Stream(device)
+    per = max(1, min(steps, max(n_items, 64)))  # calls per graph, cycling the inputs
+    full, rem = divmod(steps, per)
     torch.cuda.synchronize(device)
     with torch.cuda.stream(stream):
-        for i in range(per_graph):  # eager warm-up of every copy before capture
-            launch(wl, d, i)
+        for i in range(max(1, warmup)):
+            launch(i % n_items)
     torch.cuda.synchronize(device)
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
-        for i in range(per_graph):
-            launch(wl, d, i)
-    reps = max(1, steps // per_graph)
-    wreps = max(1, warmup // per_graph) if warmup > 0 else 0
-    with torch.cuda.stream(stream):
-        for _ in range(wreps):
-            g.replay()
-    torch.cuda.synchronize(device)
+    graphs = []
+    for count, reps in ((per, full), (rem, 1)):
+        if count and reps:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(count):
+                    launch(i % n_items)
+            graphs.append((g, reps))
+    # two untimed rehearsals of exactly the timed sequence: the first pass of
+    # it pays one-time costs (measured: 181 vs 110 us for 20 launches)
+    for _ in range(2):
+        with torch.cuda.stream(stream):
+            for g, reps in graphs:
+                for _ in range(reps):
+                    g.replay()
+        if flush:
+            flush_caches(device, stream)
+        torch.cuda.synchronize(device)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     with torch.cuda.stream(stream):
         e0.record(stream)
-        for _ in range(reps):
-            g.replay()
+        for g, reps in graphs:
+            for _ in range(reps):
+                g.replay()
         e1.record(stream)
     torch.cuda.synchronize(device)
     t1 = time.perf_counter()
-    launches = reps * per_graph
-    ev_ms = e0.elapsed_time(e1) / launches
-    wall_ms = (t1 - t0) * 1e3 / launches
-    return {"launches": launches, "event_ms": ev_ms, "wall_ms": wall_ms, "wbytes": d["wbytes"], "copies": d["copies"],
-            "data": d}
+    return e0.elapsed_time(e1) / steps, (t1 - t0) * 1e3 / steps
 
 
-def hot_time(wl, device, iters=200):
+def time_workload(wl, steps, warmup, device, rotate=True):
+    """Per-launch time (ms) of exactly `steps` launches of one workload, by
+    events on the launch stream and by the host clock, with the weight copies
+    rotated (qgemv) and the caches flushed before the timed region."""
+    d = setup(wl, device, rotate)
+    ev_ms, wall_ms = timed_calls(lambda i: launch(wl, d, i), d["copies"], steps, warmup, device, flush=rotate)
+    timed = min(d["copies"], steps)
+    cold = rotate and (steps <= d["copies"] or d["copies"] * d["wbytes"] >= 2 * MALL_BYTES)
+    return {"launches": steps, "event_ms": ev_ms, "wall_ms": wall_ms, "wbytes": d["wbytes"], "copies": d["copies"],
+            "copies_timed": timed, "footprint_bytes": timed * d["wbytes"], "cold": bool(cold), "data": d}
+
+
+def calib_read(device, nbytes, steps=2000, warmup=50):
+    """Measured streaming-read ceiling for a weight stream of nbytes: the
+    library's calibration read kernel (bsq_calib_read, the decode kernel's
+    16-byte nontemporal load form) over rotated buffers of that size, same
+    graph replay and cache flush as the timed GEMV.  Returns GB/s and us."""
+    import torch
+
+    from block_scaled_bit_e2m1_amd import bsq
+
+    nb = (nbytes + 15) // 16 * 16
+    copies = max(1, ROTATE_BYTES // nb)
+    bufs = [torch.randint(0, 1 << 30, (nb // 4,), dtype=torch.int32, device=device) for _ in range(copies)]
+    sink = torch.zeros(1, dtype=torch.float32, device=device)
+
+    def one(i):
+        st = bsq.bsq_calib_read(bsq._ptr(bufs[i]), nb, bsq._ptr(sink), bsq._stream(device))
+        assert st == bsq.OK, bsq.bsq_last_error()
+
+    ev_ms, _ = timed_calls(one, copies, steps, warmup, device)
+    del bufs
+    return {"bytes": nb, "us": round(ev_ms * 1e3, 4), "GB/s": round(nb / (ev_ms * 1e-3) / 1e9, 2),
+            "kernel": "read_kernel (bsq_calib_read)", "copies": copies}
+
+
+def calib_mfma(device, iters=20000, workgroups=1024, reps=5):
+    """Measured bf16 MFMA ceiling: the library's register-only MFMA loop
+    (bsq_calib_mfma) at 4 waves per SIMD.  Returns TFLOP/s."""
+    import torch
+
+    from block_scaled_bit_e2m1_amd import bsq
+
+    sink = torch.zeros(1, dtype=torch.float32, device=device)
+    stream = torch.cuda.Stream(device)
+    flops = float(workgroups) * 4 * iters * 4 * 32768
+
+    def one():
+        st = bsq.bsq_calib_mfma(iters, workgroups, bsq._ptr(sink), bsq._stream(device))
+        assert st == bsq.OK, bsq.bsq_last_error()
+
+    with torch.cuda.stream(stream):
+        one()
+    torch.cuda.synchronize(device)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(reps):
+            one()
+        e1.record(stream)
+    torch.cuda.synchronize(device)
+    ms = e0.elapsed_time(e1) / reps
+    return {"TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1), "kernel": "mfma_loop_kernel (bsq_calib_mfma)",
+            "flops_per_launch": flops, "ms": round(ms, 4)}
+
+
+def hot_time(wl, device, iters=2000):
     """Same launch on one resident copy (served partly from the Infinity Cache)."""
-    r = time_workload(wl, iters * 10, 50, device, rotate=False, per_graph=64)
+    r = time_workload(wl, iters, 50, device, rotate=False)
     return r["event_ms"]
 
 
@@ -365,17 +463,64 @@ def cpu_baseline(wl, budget_s=10.0):
             t_total += time.perf_counter() - t0
             reps += 1
         v = wb * reps / t_total / 1e9
-        return {"value": round(v, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-                "sample": f"{reps} full passes of {wl.name} (dequant to f32 on 1 core, then fp64 dot on "
-                          f"{threads} threads), {t_total:.1f} s", **stages}
+        used = min(threads, wl.m)  # the oracle splits its dot by activation rows: one row, one thread
+        return {"value": round(v, 4), "unit": "GB/s", "cores": used, "kind": "oracle",
+                "sample": f"{reps} full passes of {wl.name} (dequant to f32 and the fp64 dot of its one "
+                          f"activation row, {used} thread), {t_total:.1f} s", **stages}
     rows = max(1, min(wl.m, 16))
     t0 = time.perf_counter()
     wd = oracle.dequant_packed(p)
     oracle.matmul(X, wd, rows=np.arange(rows), threads=threads)
     t = time.perf_counter() - t0
     v = 2.0 * rows * wl.n * wl.k / t / 1e12
-    return {"value": round(v, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"dequant + fp64 dot of {rows} of {wl.m} rows of {wl.name}, {t:.1f} s", **stages}
+    return {"value": round(v, 6), "unit": "TFLOP/s", "cores": min(threads, rows), "kind": "oracle",
+            "sample": f"dequant (1 thread) + fp64 dot of {rows} of {wl.m} rows of {wl.name} "
+                      f"({min(threads, rows)} threads), {t:.1f} s", **stages}
+
+
+def kernel_name(wl):
+    """The kernel a workload's launch runs (as the library dispatches it)."""
+    four = wl.fmt in ("mxfp4", "nvfp4", "int4_affine")
+    if wl.op == "qgemv" and wl.act == "bf16" and wl.k % (32 if four else 16) == 0:
+        one = wl.k == 64 * (2 if four else 4) * (32 if four else 16)
+        return ("gemv1_kernel" if one else "gemv_kernel") + " (bsq_qgemv)"
+    if wl.op == "qgemm" and wl.act == "bf16" and wl.m > 8:
+        return "mfma_kernel (bsq_qgemm)"
+    return "rows_kernel (bsq_qgemv / bsq_qgemm)"
+
+
+def roofline_obj(wl, r, read_calib=None, mfma_calib=None):
+    """Roofline object of one timed workload: achieved = algorithmic bytes (or
+    flops) per launch / event-timed launch duration, against the vendor peak
+    and, where taken, the peak measured on this device by the calibration
+    kernels (same byte count / register-only MFMA loop)."""
+    kind = "qgemv" if wl.op == "qgemv" else "qgemm"
+    ev_s = r["event_ms"] * 1e-3
+    if wl.op == "qgemv":
+        io = (2 if wl.act == "bf16" else 4) * (wl.k + wl.n)
+        alg = r["wbytes"] + io
+        a = alg / ev_s / 1e9
+        o = {"bound": "hbm", "achieved": round(a, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(a / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name, kind),
+             "kernel": kernel_name(wl), "alg_bytes_per_launch": alg, "event_ms_per_launch": round(r["event_ms"], 6),
+             "event_ms_launches": r.get("steady_launches", r["launches"])}
+        if "region_event_ms" in r:
+            o["event_ms_per_step_timed_region"] = round(r["region_event_ms"], 6)
+        if read_calib:
+            w = r["wbytes"] / ev_s / 1e9  # weight stream rate, like for like with the read of the same bytes
+            o.update({"measured_peak": read_calib["GB/s"], "frac_measured": round(w / read_calib["GB/s"], 4),
+                      "measured_peak_kernel": read_calib["kernel"]})
+        return o
+    if not (wl.act == "bf16" and wl.m > 8):
+        return None  # the small f32 case is launch-latency bound: no roofline
+    a = wl.flops / ev_s / 1e12
+    o = {"bound": "mfma", "achieved": round(a, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+         "frac": round(a / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": measured_traffic(wl.name, kind),
+         "kernel": kernel_name(wl), "alg_flops_per_launch": wl.flops, "event_ms_per_launch": round(r["event_ms"], 6)}
+    if mfma_calib:
+        o.update({"measured_peak": mfma_calib["TFLOP/s"], "frac_measured": round(a / mfma_calib["TFLOP/s"], 4),
+                  "measured_peak_kernel": mfma_calib["kernel"]})
+    return o
 
 
 def main():
@@ -391,6 +536,9 @@ def main():
     ap.add_argument("--mx-pair", default="", help="with --mx-only: one pair XFMT,WFMT (e.g. mxfp4,mxfp4)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="only run torch's copy kernel on MIB MiB (counter calibration) and exit")
+    ap.add_argument("--calib-stream", action="store_true",
+                    help="only run the calibration kernels (cold streaming read of each decode workload's weight "
+                         "bytes; register-only bf16 MFMA loop) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (this build has no multi-GPU "
@@ -415,6 +563,22 @@ def main():
         return
     bsq.lib()
     warm_up(device)
+    decode = [w for w in workloads.WORKLOADS.values() if w.op == "qgemv"]
+
+    def read_calibs(steps):
+        out = {}
+        for w in decode:
+            wb = bsq.packed_bytes(w.fmt, w.n, w.k)
+            nb = sum(wb) + (4 if w.fmt == "nvfp4" else 0)
+            if nb not in out:
+                out[nb] = calib_read(device, nb, steps=steps)
+        return out
+
+    if args.calib_stream:
+        for nb, c in read_calibs(max(20, args.steps)).items():
+            print(json.dumps({"calib": "stream_read", **c}), flush=True)
+        print(json.dumps({"calib": "mfma_bf16", **calib_mfma(device)}), flush=True)
+        return
     if args.mx_only:
         pairs = [tuple(args.mx_pair.split(","))] if args.mx_pair else MX_PAIRS
         for xf, wf in pairs:
@@ -428,23 +592,37 @@ def main():
     if kind == "qgemv":
         metric, unit = HEADLINE_METRIC, "GB/s"  # value: the qgemv half of the metric
         value = r["wbytes"] / (ms * 1e-3) / 1e9
-        io_bytes = 2 * (wl.k + wl.n) if wl.act == "bf16" else 4 * (wl.k + wl.n)
-        alg = r["wbytes"] + io_bytes
-        achieved = alg / (r["event_ms"] * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name, kind),
-                "kernel": "rows_kernel (bsq_qgemv)", "alg_bytes_per_launch": alg,
-                "event_ms_per_launch": round(r["event_ms"], 6)}
     else:
         metric, unit = "TFLOP/s (qgemm)", "TFLOP/s"
         value = wl.flops / (ms * 1e-3) / 1e12
-        achieved = wl.flops / (r["event_ms"] * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": measured_traffic(wl.name, kind),
-                "kernel": "mfma_kernel (bsq_qgemm)", "alg_flops_per_launch": wl.flops,
-                "event_ms_per_launch": round(r["event_ms"], 6)}
-    log(f"  {wl.name}: {value:.1f} {unit}  ({r['event_ms'] * 1e3:.2f} us/launch by events, "
-        f"{ms * 1e3:.2f} us by host clock, {r['copies']} weight copies)")
+    log(f"  {wl.name}: {value:.1f} {unit}  ({r['event_ms'] * 1e3:.2f} us/step by events, {ms * 1e3:.2f} us/step "
+        f"by host clock over the {r['launches']} timed steps, {r['copies_timed']} weight copies timed, cold={r['cold']})")
+    # The launch duration of the roofline: the same launches, rotation and cache
+    # flush over a region long enough that the graph's start on the device
+    # (tens of us, paid once per region) does not count as kernel time.
+    rs = r if args.steps >= STEADY_STEPS else time_workload(wl, STEADY_STEPS, args.warmup, device)
+    r["region_event_ms"] = r["event_ms"]
+    r["event_ms"] = rs["event_ms"]
+    r["steady_launches"] = rs["launches"]
+    log(f"  {wl.name}: {r['event_ms'] * 1e3:.2f} us/launch by events over {rs['launches']} launches")
+
+    calib = None
+    if not args.only_timed:
+        rc = read_calibs(2000)
+        mc = calib_mfma(device)
+        calib = {"stream_read": list(rc.values()), "mfma_bf16": mc}
+        for c in rc.values():
+            log(f"  calibration read {c['bytes']} B: {c['us']:.2f} us, {c['GB/s']:.0f} GB/s")
+        log(f"  calibration bf16 MFMA loop: {mc['TFLOP/s']:.0f} TFLOP/s")
+
+    def calib_for(w2):
+        if calib is None:
+            return None, None
+        wb = sum(bsq.packed_bytes(w2.fmt, w2.n, w2.k)) + (4 if w2.fmt == "nvfp4" else 0)
+        rd = next((c for c in calib["stream_read"] if c["bytes"] == (wb + 15) // 16 * 16), None)
+        return rd, calib["mfma_bf16"]
+
+    roof = roofline_obj(wl, r, *calib_for(wl))
 
     extra = []
     if not args.no_extra and not args.only_timed:
@@ -459,12 +637,12 @@ def main():
             r2 = time_workload(w2, steps, steps // 10, device)
             if w2.op == "qgemv":
                 v, u = r2["wbytes"] / (r2["event_ms"] * 1e-3) / 1e9, "GB/s"
-                fr = v / HBM_PEAK_GBS
             else:
                 v, u = w2.flops / (r2["event_ms"] * 1e-3) / 1e12, "TFLOP/s"
-                fr = v / MFMA_BF16_PEAK_TFLOPS if w2.act == "bf16" and w2.m > 8 else None
+            ro = roofline_obj(w2, r2, *calib_for(w2))
             e = {"workload": name, "value": round(v, 3), "unit": u, "us_per_launch": round(r2["event_ms"] * 1e3, 3),
-                 "roofline_frac": None if fr is None else round(fr, 4)}
+                 "roofline_frac": None if ro is None else ro["frac"], "roofline": ro,
+                 "weight_copies_timed": r2["copies_timed"], "cold": r2["cold"]}
             extra.append(e)
             log(f"  {name}: {v:.2f} {u} ({r2['event_ms'] * 1e3:.2f} us/launch)")
             del r2
@@ -492,14 +670,16 @@ def main():
         "vs_baseline": None, "dtype": "bf16" if wl.act == "bf16" else "f32",
         "data": "synthetic (seeded N(0,sigma) weights, N(0,1) activations)",
         "config": {"workload": wl.name, "format": wl.fmt, "m": wl.m, "n": wl.n, "k": wl.k,
-                   "weight_copies_rotated": r["copies"], "graph_replay": True},
-        "roofline": roof, "cpu_baseline": cpu, "extra": extra,
+                   "weight_copies": r["copies"], "weight_copies_timed": r["copies_timed"],
+                   "timed_footprint_bytes": r["footprint_bytes"], "caches_flushed_before_timing": True,
+                   "cold_hbm_reads": r["cold"], "graph_replay": True},
+        "roofline": roof, "cpu_baseline": cpu, "calibration": calib, "extra": extra,
     }
     gemm = [e for e in extra if e.get("workload") == "mxfp4_qgemm_2048" and e.get("unit") == "TFLOP/s"]
     if gemm:
         line["qgemm_m2048"] = {"workload": "mxfp4_qgemm_2048", "value": gemm[0]["value"], "unit": "TFLOP/s",
                                "us_per_launch": gemm[0]["us_per_launch"], "roofline_frac": gemm[0]["roofline_frac"],
-                               "peak": MFMA_BF16_PEAK_TFLOPS}
+                               "peak": MFMA_BF16_PEAK_TFLOPS, "roofline": gemm[0]["roofline"]}
     print(json.dumps(line), flush=True)
 
 

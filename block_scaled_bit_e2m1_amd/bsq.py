@@ -32,7 +32,8 @@ PATH_AUTO, PATH_ROWS, PATH_MFMA = 0, 1, 2
 OK, ERR_ARG, ERR_UNSUPPORTED, ERR_SHAPE, ERR_ALIGN, ERR_NONFINITE, ERR_HIP = 0, 1, 2, 3, 4, 5, 6
 
 EXPORTS = ["bsq_packed_bytes", "bsq_pack_host", "bsq_quantize", "bsq_dequant", "bsq_qgemv", "bsq_qgemm", "bsq_qgemm_path",
-           "bsq_qgemm_mx", "bsq_rmsnorm_qgemv", "bsq_gather_qmm", "bsq_status_string", "bsq_last_error", "bsq_version"]
+           "bsq_qgemm_mx", "bsq_rmsnorm_qgemv", "bsq_gather_qmm", "bsq_calib_read", "bsq_calib_mfma",
+           "bsq_status_string", "bsq_last_error", "bsq_version"]
 
 
 class BsqError(RuntimeError):
@@ -64,8 +65,10 @@ def lib() -> ctypes.CDLL:
                                         _vp, _c_int, _vp]
         L.bsq_gather_qmm.argtypes = [_c_int, _c_int, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _f32, _vp, _vp, _c_int, _vp,
                                      _c_int, _vp, _vp]
+        L.bsq_calib_read.argtypes = [_vp, _i64, _vp, _vp]
+        L.bsq_calib_mfma.argtypes = [_i64, _i64, _vp, _vp]
         for f in ("bsq_packed_bytes", "bsq_pack_host", "bsq_quantize", "bsq_dequant", "bsq_qgemv", "bsq_qgemm", "bsq_qgemm_path",
-                  "bsq_qgemm_mx", "bsq_rmsnorm_qgemv", "bsq_gather_qmm"):
+                  "bsq_qgemm_mx", "bsq_rmsnorm_qgemv", "bsq_gather_qmm", "bsq_calib_read", "bsq_calib_mfma"):
             getattr(L, f).restype = _c_int
         for f in ("bsq_status_string", "bsq_last_error", "bsq_version"):
             getattr(L, f).restype = ctypes.c_char_p
@@ -117,6 +120,14 @@ def bsq_gather_qmm(fmt, block, m, n, k, num_experts, codes, scales, biases, glob
                    status_dev, stream):
     return lib().bsq_gather_qmm(fmt, block, m, n, k, num_experts, codes, scales, biases, global_scale, expert_ids, x,
                                 xt, out, ot, status_dev, stream)
+
+
+def bsq_calib_read(buf, nbytes, sink, stream):
+    return lib().bsq_calib_read(buf, nbytes, sink, stream)
+
+
+def bsq_calib_mfma(iters, workgroups, sink, stream):
+    return lib().bsq_calib_mfma(iters, workgroups, sink, stream)
 
 
 def bsq_qgemm_path(path, fmt, block, m, n, k, codes, scales, biases, global_scale, x, xt, out, ot, stream):

@@ -250,6 +250,21 @@ bsq_status bsq_gather_qmm(bsq_format fmt, int block, int64_t m, int64_t n, int64
                     "gather launch");
 }
 
+bsq_status bsq_calib_read(const void *buf, int64_t bytes, float *sink, void *stream) {
+  if (bytes < 0) return fail(BSQ_ERR_ARG, "negative size");
+  if (bytes % 16) return fail(BSQ_ERR_SHAPE, "bytes=%lld is not a multiple of 16", (long long)bytes);
+  if (bytes == 0) return ok();
+  if (!buf || !sink) return fail(BSQ_ERR_ARG, "null buffer or sink");
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return fail(BSQ_ERR_ALIGN, "buf must be 16-byte aligned");
+  return hip_status(bsq::launch_calib_read(buf, bytes, sink, (hipStream_t)stream), "calib read launch");
+}
+
+bsq_status bsq_calib_mfma(int64_t iters, int64_t workgroups, float *sink, void *stream) {
+  if (iters < 0 || workgroups < 1 || workgroups > 0x7FFFFFFF) return fail(BSQ_ERR_ARG, "bad iters or workgroups");
+  if (!sink || !aligned(sink, 4)) return fail(BSQ_ERR_ARG, "null or misaligned sink");
+  return hip_status(bsq::launch_calib_mfma(iters, workgroups, sink, (hipStream_t)stream), "calib mfma launch");
+}
+
 const char *bsq_status_string(bsq_status s) {
   switch (s) {
     case BSQ_OK: return "ok";

@@ -79,6 +79,11 @@ hipError_t launch_quantize(int fmt, const void *w, int wt, int64_t n, int64_t k,
 hipError_t launch_mxmma(int xfmt, const void *xc, const void *xs, int wfmt, const void *wc, const void *ws, int64_t m,
                         int64_t n, int64_t k, void *out, int ot, hipStream_t s);
 
+// Calibration kernels (calib.hip): streaming read of `bytes` (a multiple of
+// 16) and a register-only bf16 MFMA loop.
+hipError_t launch_calib_read(const void *buf, int64_t bytes, float *sink, hipStream_t s);
+hipError_t launch_calib_mfma(int64_t iters, int64_t workgroups, float *sink, hipStream_t s);
+
 // Host packer (pack_host.cpp).  Returns a bsq_status value.
 int pack_host(int fmt, const float *w, int64_t n, int64_t k, void *codes, void *scales, void *biases,
               float *global_out);

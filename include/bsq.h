@@ -195,6 +195,24 @@ bsq_status bsq_gather_qmm(bsq_format fmt, int block, int64_t m, int64_t n, int64
                           const int32_t *expert_ids, const void *x, bsq_dtype xt, void *out, bsq_dtype ot,
                           int *status_dev, void *stream);
 
+/* Calibration (measurement only; not a step of the hot path).  A streaming
+ * read of `bytes` bytes of the device buffer `buf` with the decode kernel's
+ * load form (one 16-byte nontemporal load per lane, each byte read once,
+ * nothing kept): the bandwidth a weight stream of that size reaches on this
+ * device, the measured denominator beside the vendor HBM figure.  buf 16-byte
+ * aligned, bytes >= 0 and a multiple of 16 (BSQ_ERR_ALIGN / BSQ_ERR_SHAPE);
+ * sink: device float, written only for data whose four words XOR to one
+ * fixed constant (so the loads cannot be dropped).  Asynchronous on stream. */
+bsq_status bsq_calib_read(const void *buf, int64_t bytes, float *sink, void *stream);
+
+/* Calibration: `workgroups` workgroups of 4 waves; each wave runs `iters`
+ * steps of four independent v_mfma_f32_32x32x16_bf16 on register operands
+ * (no memory traffic).  Work = workgroups * 4 * iters * 4 * 32768 flops; the
+ * bf16 matrix-core rate this device sustains, beside the vendor figure.
+ * iters >= 0, 1 <= workgroups < 2^31 (BSQ_ERR_ARG); sink: device float.
+ * Asynchronous on stream. */
+bsq_status bsq_calib_mfma(int64_t iters, int64_t workgroups, float *sink, void *stream);
+
 /* Static text for a status code. */
 const char *bsq_status_string(bsq_status s);
 

@@ -82,6 +82,15 @@ def test_validation_errors():
     assert bsq.bsq_qgemv(bsq.MXFP4, 0, 0, 64, None, None, null, 1.0, None, bsq.BF16, None, bsq.BF16, null) == bsq.OK
     assert bsq.bsq_dequant(bsq.MXFP4, 0, 0, 64, None, None, null, 1.0, None, null) == bsq.OK
     assert "aligned" in bsq.bsq_last_error() or bsq.bsq_last_error() == ""
+    # calibration entry points: validation before any launch
+    assert bsq.bsq_calib_read(p, 40, p, null) == bsq.ERR_SHAPE
+    assert bsq.bsq_calib_read(p, -16, p, null) == bsq.ERR_ARG
+    assert bsq.bsq_calib_read(mis, 64, p, null) == bsq.ERR_ALIGN
+    assert bsq.bsq_calib_read(None, 64, p, null) == bsq.ERR_ARG
+    assert bsq.bsq_calib_read(None, 0, None, null) == bsq.OK
+    assert bsq.bsq_calib_mfma(10, 0, p, null) == bsq.ERR_ARG
+    assert bsq.bsq_calib_mfma(-1, 4, p, null) == bsq.ERR_ARG
+    assert bsq.bsq_calib_mfma(10, 4, None, null) == bsq.ERR_ARG
 
 
 def test_pack_rejects_nonfinite():
