@@ -19,7 +19,7 @@ for the timed kernel, and the CPU oracle timed on a bounded sample as
 `cpu_baseline`.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-extra] [--no-cpu] [--only-timed]
+                    [--no-extra] [--no-cpu] [--only-timed] [--mx-only] [--grouped-only]
 """
 from __future__ import annotations
 
@@ -50,6 +50,7 @@ KERNEL_SOURCES = {"qgemv": ["block_scaled_bit_e2m1_amd/csrc/gemv.hip", "block_sc
                             "block_scaled_bit_e2m1_amd/csrc/epilogue.hpp"],
                   "qgemm_mx": ["block_scaled_bit_e2m1_amd/csrc/mxmma.hip", "block_scaled_bit_e2m1_amd/csrc/codec.hpp",
                                "block_scaled_bit_e2m1_amd/csrc/epilogue.hpp"]}
+KERNEL_SOURCES["grouped"] = ["block_scaled_bit_e2m1_amd/csrc/grouped.hip"] + KERNEL_SOURCES["qgemm"]
 MX_PAIRS = [("mxfp4", "mxfp4"), ("mxfp8_e4m3", "mxfp4"), ("mxfp8_e4m3", "mxfp8_e4m3")]
 # The headline metric has two halves: the m = 1 decode GEMV's weight stream
 # (the line's value) and the m = 2048 prefill GEMM's TFLOP/s (reported beside it).
@@ -401,6 +402,41 @@ def time_gather_qmm(device, fmt="mxfp4", E=8, n=14336, k=4096, ids=(1, 6, 2, 5))
             "roofline_frac": round(wb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def time_grouped_qmm(device, name="mxfp4_moe_prefill_8x4096", reps=200):
+    """Prefill MoE step (bsq_grouped_qgemm): the routing kernel, then the
+    grouped MFMA GEMM over 128-row tiles of each expert's rows, bf16 out.  One
+    expert stack (its 71 MB stay in the Infinity Cache across launches; the
+    step is bound by the matrix cores, not HBM).  Rate = 2*m*n*k / time."""
+    import numpy as np
+    import torch
+
+    from block_scaled_bit_e2m1_amd import bsq, workloads
+
+    wl = workloads.MOE_WORKLOADS[name]
+    W, X, ids = workloads.generate_moe(wl)
+    stack = bsq.to_device(bsq.pack(wl.fmt, W), device)
+    del W
+    x = torch.from_numpy(X).to(torch.bfloat16).to(device)
+    eids = torch.from_numpy(ids).to(device)
+    st, need = bsq.bsq_grouped_qgemm_workspace(wl.m, wl.experts)
+    assert st == bsq.OK
+    ws = torch.empty(need, dtype=torch.uint8, device=device)
+    out = torch.empty((wl.m, wl.n), dtype=torch.bfloat16, device=device)
+    ms = graph_event_ms(lambda: bsq.grouped_qmm(stack, wl.experts, eids, x, out=out, workspace=ws), 4,
+                        max(1, reps // 4), device)
+    tf = wl.flops / (ms * 1e-3) / 1e12
+    rows = np.bincount(ids, minlength=wl.experts)
+    roof = {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": measured_traffic(name, "grouped"),
+            "kernel": "route_kernel + mfma_kernel (bsq_grouped_qgemm)", "alg_flops_per_launch": wl.flops,
+            "event_ms_per_launch": round(ms, 6)}
+    return {"workload": name, "note": f"prefill MoE: {wl.tokens} tokens top-{wl.topk} of {wl.experts} {wl.fmt} "
+            f"experts of {wl.n}x{wl.k}, rows grouped by expert on the device (bsq_grouped_qgemm)",
+            "value": round(tf, 2), "unit": "TFLOP/s", "us_per_launch": round(ms * 1e3, 3),
+            "roofline_frac": roof["frac"], "roofline": roof, "expert_rows": rows.tolist(),
+            "tiles": int(sum((c + 127) // 128 for c in rows))}
+
+
 def warm_up(device, seconds=0.5):
     """Keep the GPU busy for a moment before anything is timed, so the first
     measurement does not run on a cold clock (measured: the first timing of a
@@ -533,6 +569,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only-timed", action="store_true", help="timed workload only (for profiling)")
     ap.add_argument("--mx-only", action="store_true", help="only time the scaled-MFMA GEMMs and exit")
+    ap.add_argument("--grouped-only", action="store_true", help="only time the prefill MoE grouped GEMM and exit")
     ap.add_argument("--mx-pair", default="", help="with --mx-only: one pair XFMT,WFMT (e.g. mxfp4,mxfp4)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="only run torch's copy kernel on MIB MiB (counter calibration) and exit")
@@ -583,6 +620,9 @@ def main():
         pairs = [tuple(args.mx_pair.split(","))] if args.mx_pair else MX_PAIRS
         for xf, wf in pairs:
             print(json.dumps(time_qgemm_mx(device, xf, wf, reps=max(1, args.steps // 8))), flush=True)
+        return
+    if args.grouped_only:
+        print(json.dumps(time_grouped_qmm(device, reps=max(4, args.steps))), flush=True)
         return
     wl = workloads.WORKLOADS[args.workload]
     kind = "qgemv" if wl.op == "qgemv" else "qgemm"
@@ -653,6 +693,10 @@ def main():
         for e in (time_rmsnorm_qgemv(device), time_gather_qmm(device)):
             extra.append(e)
             log(f"  {e['workload']}: {e['value']:.1f} GB/s ({e['us_per_launch']:.2f} us/launch)")
+        e = time_grouped_qmm(device)
+        extra.append(e)
+        log(f"  {e['workload']}: {e['value']:.1f} TFLOP/s ({e['us_per_launch']:.2f} us/launch)")
+        torch.cuda.empty_cache()
         for xf, wf in MX_PAIRS:
             e = time_qgemm_mx(device, xf, wf)
             extra.append(e)

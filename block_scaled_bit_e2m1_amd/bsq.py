@@ -32,7 +32,8 @@ PATH_AUTO, PATH_ROWS, PATH_MFMA = 0, 1, 2
 OK, ERR_ARG, ERR_UNSUPPORTED, ERR_SHAPE, ERR_ALIGN, ERR_NONFINITE, ERR_HIP = 0, 1, 2, 3, 4, 5, 6
 
 EXPORTS = ["bsq_packed_bytes", "bsq_pack_host", "bsq_quantize", "bsq_dequant", "bsq_qgemv", "bsq_qgemm", "bsq_qgemm_path",
-           "bsq_qgemm_mx", "bsq_rmsnorm_qgemv", "bsq_gather_qmm", "bsq_calib_read", "bsq_calib_mfma",
+           "bsq_qgemm_mx", "bsq_rmsnorm_qgemv", "bsq_gather_qmm", "bsq_grouped_qgemm_workspace", "bsq_grouped_qgemm",
+           "bsq_calib_read", "bsq_calib_mfma",
            "bsq_status_string", "bsq_last_error", "bsq_version"]
 
 
@@ -65,10 +66,14 @@ def lib() -> ctypes.CDLL:
                                         _vp, _c_int, _vp]
         L.bsq_gather_qmm.argtypes = [_c_int, _c_int, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _f32, _vp, _vp, _c_int, _vp,
                                      _c_int, _vp, _vp]
+        L.bsq_grouped_qgemm_workspace.argtypes = [_i64, _i64, _sz]
+        L.bsq_grouped_qgemm.argtypes = [_c_int, _c_int, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _f32, _vp, _vp, _vp,
+                                        _c_int, _vp, ctypes.c_size_t, _vp, _vp]
         L.bsq_calib_read.argtypes = [_vp, _i64, _vp, _vp]
         L.bsq_calib_mfma.argtypes = [_i64, _i64, _vp, _vp]
         for f in ("bsq_packed_bytes", "bsq_pack_host", "bsq_quantize", "bsq_dequant", "bsq_qgemv", "bsq_qgemm", "bsq_qgemm_path",
-                  "bsq_qgemm_mx", "bsq_rmsnorm_qgemv", "bsq_gather_qmm", "bsq_calib_read", "bsq_calib_mfma"):
+                  "bsq_qgemm_mx", "bsq_rmsnorm_qgemv", "bsq_gather_qmm", "bsq_grouped_qgemm_workspace",
+                  "bsq_grouped_qgemm", "bsq_calib_read", "bsq_calib_mfma"):
             getattr(L, f).restype = _c_int
         for f in ("bsq_status_string", "bsq_last_error", "bsq_version"):
             getattr(L, f).restype = ctypes.c_char_p
@@ -120,6 +125,18 @@ def bsq_gather_qmm(fmt, block, m, n, k, num_experts, codes, scales, biases, glob
                    status_dev, stream):
     return lib().bsq_gather_qmm(fmt, block, m, n, k, num_experts, codes, scales, biases, global_scale, expert_ids, x,
                                 xt, out, ot, status_dev, stream)
+
+
+def bsq_grouped_qgemm_workspace(m, num_experts):
+    n = ctypes.c_size_t(0)
+    st = lib().bsq_grouped_qgemm_workspace(m, num_experts, ctypes.byref(n))
+    return st, n.value
+
+
+def bsq_grouped_qgemm(fmt, block, m, n, k, num_experts, codes, scales, biases, global_scale, expert_ids, x, out, ot,
+                      workspace, workspace_bytes, status_dev, stream):
+    return lib().bsq_grouped_qgemm(fmt, block, m, n, k, num_experts, codes, scales, biases, global_scale, expert_ids,
+                                   x, out, ot, workspace, workspace_bytes, status_dev, stream)
 
 
 def bsq_calib_read(buf, nbytes, sink, stream):
@@ -306,6 +323,36 @@ def gather_qmm(stack: PackedWeight, num_experts: int, expert_ids: torch.Tensor, 
                         _ptr(stack.biases), stack.global_scale, _ptr(expert_ids), _ptr(x), _DT[x.dtype], _ptr(out),
                         _DT[out.dtype], _ptr(status), _stream(dev))
     _check(st, "bsq_gather_qmm")
+    return out
+
+
+def grouped_qmm(stack: PackedWeight, num_experts: int, expert_ids: torch.Tensor, x: torch.Tensor,
+                out: torch.Tensor | None = None, out_dtype=None, status: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """The routed gather's result with the rows grouped by expert on the
+    device (bsq_grouped_qgemm): x bf16 [m, k], one int32 expert id per row,
+    stack packed as one [num_experts*n, k] weight.  `workspace` (a uint8 device
+    tensor of at least bsq_grouped_qgemm_workspace bytes) is allocated here
+    when not given."""
+    if stack.n % num_experts:
+        raise ValueError("stack rows must be num_experts * n")
+    n = stack.n // num_experts
+    m = x.shape[0]
+    if expert_ids.dtype != torch.int32 or expert_ids.numel() != m:
+        raise ValueError("expert_ids must be int32 with one id per x row")
+    if x.dtype != torch.bfloat16:
+        raise ValueError("grouped_qmm takes bf16 activations")
+    dev = stack.codes.device
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype or x.dtype, device=dev)
+    st, need = bsq_grouped_qgemm_workspace(m, num_experts)
+    _check(st, "bsq_grouped_qgemm_workspace")
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
+    st = bsq_grouped_qgemm(stack.fmt, 0, m, n, stack.k, num_experts, _ptr(stack.codes), _ptr(stack.scales),
+                           _ptr(stack.biases), stack.global_scale, _ptr(expert_ids), _ptr(x), _ptr(out),
+                           _DT[out.dtype], _ptr(workspace), workspace.numel(), _ptr(status), _stream(dev))
+    _check(st, "bsq_grouped_qgemm")
     return out
 
 

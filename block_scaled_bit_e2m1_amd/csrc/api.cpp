@@ -250,6 +250,47 @@ bsq_status bsq_gather_qmm(bsq_format fmt, int block, int64_t m, int64_t n, int64
                     "gather launch");
 }
 
+bsq_status bsq_grouped_qgemm_workspace(int64_t m, int64_t num_experts, size_t *bytes) {
+  if (m < 0 || num_experts < 1 || !bytes) return fail(BSQ_ERR_ARG, "bad m, num_experts or null bytes");
+  if (num_experts > bsq::kMaxExperts || m > ((int64_t)1 << 24))
+    return fail(BSQ_ERR_SHAPE, "num_experts <= %d and m <= 2^24", bsq::kMaxExperts);
+  *bytes = (size_t)bsq::grouped_workspace_bytes(m, num_experts);
+  return ok();
+}
+
+bsq_status bsq_grouped_qgemm(bsq_format fmt, int block, int64_t m, int64_t n, int64_t k, int64_t num_experts,
+                             const void *codes, const void *scales, const void *biases, float global_scale,
+                             const int32_t *expert_ids, const void *x, void *out, bsq_dtype ot, void *workspace,
+                             size_t workspace_bytes, int *status_dev, void *stream) {
+  bsq_status s;
+  if ((s = check_format(fmt, block))) return s;
+  if (num_experts < 1) return fail(BSQ_ERR_ARG, "num_experts must be >= 1");
+  if (num_experts > bsq::kMaxExperts) return fail(BSQ_ERR_SHAPE, "at most %d experts", bsq::kMaxExperts);
+  if (n < 0 || n > ((int64_t)1 << 40) / num_experts) return fail(BSQ_ERR_SHAPE, "n * num_experts out of range");
+  if ((s = check_shape(fmt, n * num_experts, k))) return s;
+  if (m < 0) return fail(BSQ_ERR_ARG, "negative m");
+  if (m > ((int64_t)1 << 24)) return fail(BSQ_ERR_SHAPE, "m=%lld: at most 2^24 rows", (long long)m);
+  if (ot != BSQ_F32 && ot != BSQ_BF16) return fail(BSQ_ERR_ARG, "bad out dtype %d", (int)ot);
+  if (bsq::is_4bit(fmt) && k % 32) return fail(BSQ_ERR_SHAPE, "k=%lld: 4-bit formats need k %% 32 == 0 here", (long long)k);
+  if (m == 0 || n == 0) return ok();
+  if (!out) return fail(BSQ_ERR_ARG, "null out");
+  if (!aligned(out, ot == BSQ_F32 ? 4 : 2)) return fail(BSQ_ERR_ALIGN, "out misaligned");
+  hipStream_t st = (hipStream_t)stream;
+  if (k == 0) return hip_status(bsq::launch_zero(out, m * n * (ot == BSQ_F32 ? 4 : 2), st), "zero-fill");
+  if ((s = check_weight(fmt, n * num_experts, k, codes, scales, biases))) return s;
+  if (!x || !expert_ids) return fail(BSQ_ERR_ARG, "null x or expert_ids");
+  if (!aligned(x, 16) || !aligned(expert_ids, 4)) return fail(BSQ_ERR_ALIGN, "x (16) or expert_ids (4) misaligned");
+  if (status_dev && !aligned(status_dev, 4)) return fail(BSQ_ERR_ALIGN, "status misaligned");
+  if (m > ((int64_t)1 << 40) / k) return fail(BSQ_ERR_SHAPE, "m*k too large");
+  const int64_t need = bsq::grouped_workspace_bytes(m, num_experts);
+  if (!workspace || (int64_t)workspace_bytes < need)
+    return fail(BSQ_ERR_ARG, "workspace of %lld bytes needed", (long long)need);
+  if (!aligned(workspace, 4)) return fail(BSQ_ERR_ALIGN, "workspace must be 4-byte aligned");
+  const bsq::QWeight w{(int)fmt, n, k, codes, scales, biases, global_scale};
+  return hip_status(bsq::launch_grouped(w, m, num_experts, expert_ids, x, out, (int)ot, workspace, status_dev, st),
+                    "grouped launch");
+}
+
 bsq_status bsq_calib_read(const void *buf, int64_t bytes, float *sink, void *stream) {
   if (bytes < 0) return fail(BSQ_ERR_ARG, "negative size");
   if (bytes % 16) return fail(BSQ_ERR_SHAPE, "bytes=%lld is not a multiple of 16", (long long)bytes);

@@ -79,6 +79,18 @@ hipError_t launch_quantize(int fmt, const void *w, int wt, int64_t n, int64_t k,
 hipError_t launch_mxmma(int xfmt, const void *xc, const void *xs, int wfmt, const void *wc, const void *ws, int64_t m,
                         int64_t n, int64_t k, void *out, int ot, hipStream_t s);
 
+// Expert-grouped GEMM (grouped.hip): bf16 X [m,k], expert ids [m], a stacked
+// [E*n, k] weight (w.n = n, the rows of one expert); workspace of
+// grouped_workspace_bytes(m, E) bytes holds the routing table.
+constexpr int kMaxExperts = 1024;
+int64_t grouped_workspace_bytes(int64_t m, int64_t nexp);
+hipError_t launch_grouped(const QWeight &w, int64_t m, int64_t nexp, const int32_t *eids, const void *x, void *out,
+                          int ot, void *workspace, int *status, hipStream_t s);
+// The grouped form of the MFMA kernel (mfma.hip) over a routing table: gtab[0]
+// tiles, (expert, first row, row end) per tile, tokens at gtab + gperm.
+hipError_t launch_mfma_grouped(const QWeight &w, int64_t m, const void *x, void *out, int ot, const int32_t *gtab,
+                               int64_t gperm, int tiles_m, hipStream_t s);
+
 // Calibration kernels (calib.hip): streaming read of `bytes` (a multiple of
 // 16) and a register-only bf16 MFMA loop.
 hipError_t launch_calib_read(const void *buf, int64_t bytes, float *sink, hipStream_t s);

@@ -30,7 +30,8 @@ template <int WTN, int NW> constexpr int stage_bytes() { return NW * 32 * row_st
 
 template <int MT, int NT, int WTN, int ES>
 __device__ __forceinline__ void store_es(const f32x16_t (&acc)[MT][NT], float scale, uint8_t *st, int lane,
-                                         int64_t r0, int64_t c0, int64_t m, int64_t n, void *out) {
+                                         int64_t r0, int64_t c0, int64_t m, int64_t n, void *out,
+                                         const int32_t *rowmap) {
   constexpr int EV = 16 / ES;                // elements per 16-byte piece
   constexpr int RS = row_stride<WTN, ES>();  // staged row stride
   constexpr int LPR = WTN * ES / 16;         // lanes per staged row
@@ -58,7 +59,8 @@ __device__ __forceinline__ void store_es(const f32x16_t (&acc)[MT][NT], float sc
       const u32x4_t val = *reinterpret_cast<const u32x4_t *>(st + r * RS + lc * ES);
       const int64_t gr = r0 + i * 32 + r;
       if (gr >= m) continue;
-      uint8_t *dst = reinterpret_cast<uint8_t *>(out) + (gr * n + gc) * ES;
+      const int64_t orow = rowmap ? (int64_t)rowmap[gr] : gr;
+      uint8_t *dst = reinterpret_cast<uint8_t *>(out) + (orow * n + gc) * ES;
       if (vec && gc + EV <= n) {
         *reinterpret_cast<u32x4_t *>(dst) = val;
       } else {
@@ -79,12 +81,15 @@ __device__ __forceinline__ void store_es(const f32x16_t (&acc)[MT][NT], float sc
 // acc: this wave's MT x NT tiles; the wave's output block starts at row r0,
 // column c0; stage: this wave's own LDS region.  Every wave of the workgroup
 // must call it (it synchronizes the workgroup once per band).  ot: 0 = f32,
-// 1 = bf16.  Each value is multiplied by scale before rounding.
+// 1 = bf16.  Each value is multiplied by scale before rounding.  Rows at or
+// past m are not written; rowmap (may be null) sends row r to output row
+// rowmap[r] (the expert-grouped GEMM's token rows).
 template <int MT, int NT, int WTN>
 __device__ __forceinline__ void store_acc(const f32x16_t (&acc)[MT][NT], float scale, uint8_t *stage, int lane,
-                                          int64_t r0, int64_t c0, int64_t m, int64_t n, void *out, int ot) {
-  if (ot == 0) store_es<MT, NT, WTN, 4>(acc, scale, stage, lane, r0, c0, m, n, out);
-  else store_es<MT, NT, WTN, 2>(acc, scale, stage, lane, r0, c0, m, n, out);
+                                          int64_t r0, int64_t c0, int64_t m, int64_t n, void *out, int ot,
+                                          const int32_t *rowmap = nullptr) {
+  if (ot == 0) store_es<MT, NT, WTN, 4>(acc, scale, stage, lane, r0, c0, m, n, out, rowmap);
+  else store_es<MT, NT, WTN, 2>(acc, scale, stage, lane, r0, c0, m, n, out, rowmap);
 }
 
 }  // namespace epi

@@ -332,11 +332,17 @@ struct Slot {
   WRaw w[NT];
 };
 
-template <int F, int BM, int BN, int WGM, int WGN, int D, int UK, bool VEC, bool ROT, int SCHED, int DX, bool TS>
+// GRP (expert-grouped rows): gtab is the routing table the route kernel
+// built: gtab[0] tiles in use, then per m-tile (expert, first row, row limit)
+// in the sorted row order, and at gtab + gperm the token of every sorted row.
+// A tile's X rows are gathered through it, its weight rows are its expert's
+// rows of the stacked [E*n, k] weight, and its output rows are scattered back.
+template <int F, int BM, int BN, int WGM, int WGN, int D, int UK, bool VEC, bool ROT, int SCHED, int DX, bool TS,
+          bool GRP = false>
 __global__ void __launch_bounds__(WGM *WGN * 64)
 mfma_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, const uint16_t *__restrict__ biases,
             float global, const uint16_t *__restrict__ x, void *__restrict__ out, int ot, int64_t m, int64_t n,
-            int64_t k, int tiles_m, int tiles_n) {
+            int64_t k, int tiles_m, int tiles_n, const int32_t *__restrict__ gtab, int64_t gperm) {
   constexpr int NTHR = WGM * WGN * 64;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int MT = WTM / 32, NT = WTN / 32;
@@ -360,7 +366,17 @@ mfma_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
   int t = blockIdx.x;
   if ((T & 7) == 0) t = (t & 7) * (T >> 3) + (t >> 3);
   const int tm = t / tiles_n, tn = t - tm * tiles_n;
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  int64_t m0 = (int64_t)tm * BM, mlim = m, wrow0 = 0;  // first row, row limit, first weight row
+  const int32_t *perm = nullptr;
+  if constexpr (GRP) {
+    if (tm >= gtab[0]) return;  // uniform: a tile past those the routing produced
+    const int32_t *tile = gtab + 1 + 3 * tm;
+    wrow0 = (int64_t)tile[0] * n;
+    m0 = tile[1];
+    mlim = tile[2];
+    perm = gtab + gperm;
+  }
+  const int64_t n0 = (int64_t)tn * BN;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid / WGN, wn = wid - (wid / WGN) * WGN;
@@ -372,13 +388,14 @@ mfma_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
   for (int c = 0; c < XCH; ++c) {
     const int cid = c * NTHR + tid;
     const int64_t gr = m0 + (cid >> 3);
-    xp[c] = x + (gr < m ? gr : m - 1) * k + (cid & 7) * 8;  // rows past m read a valid row; never stored
+    const int64_t row = gr < mlim ? gr : mlim - 1;  // rows past the limit read a valid row; never stored
+    xp[c] = x + (GRP ? (int64_t)perm[row] : row) * k + (cid & 7) * 8;
   }
   int64_t wcol[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     const int64_t gc = n0 + wn * WTN + j * 32 + l32;
-    wcol[j] = gc < n ? gc : n - 1;
+    wcol[j] = wrow0 + (gc < n ? gc : n - 1);
   }
 
   f32x16_t acc[MT][NT];
@@ -748,12 +765,20 @@ mfma_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
   __syncthreads();
   epi::store_acc<MT, NT, WTN>(acc, F == kNVFP4 ? global : 1.0f,
                               reinterpret_cast<uint8_t *>(smem) + wid * 32 * epi::row_stride<WTN, 4>(), lane,
-                              m0 + wm * WTM, n0 + wn * WTN, m, n, out, ot);
+                              m0 + wm * WTM, n0 + wn * WTN, mlim, n, out, ot, perm);
 }
 
+// Grouped launch: tiles_m is the most m-tiles the routing can produce, gtab /
+// gperm the routing table (null for an ordinary launch).
+struct Grp {
+  const int32_t *gtab = nullptr;
+  int64_t gperm = 0;
+  int tiles_m = 0;
+};
+
 template <int F, int BM, int BN, int WGM, int WGN, int D, int UK, bool ROT = false, int SCHED = 1, int DX = 1>
-hipError_t run_cfg(const QWeight &w, int64_t m, const void *x, void *out, int ot, hipStream_t s) {
-  const int tiles_m = (int)((m + BM - 1) / BM), tiles_n = (int)((w.n + BN - 1) / BN);
+hipError_t run_cfg(const QWeight &w, int64_t m, const void *x, void *out, int ot, hipStream_t s, const Grp &g = Grp()) {
+  const int tiles_m = g.gtab ? g.tiles_m : (int)((m + BM - 1) / BM), tiles_n = (int)((w.n + BN - 1) / BN);
   const dim3 grid((unsigned)(tiles_m * tiles_n));
   const bool vec = Traits<F>::kBits == 8 || (w.k % 32) == 0;
   constexpr bool kTripOk = SCHED == 5 && UK == 4 && !ROT && kTripSc<F>;
@@ -761,15 +786,24 @@ hipError_t run_cfg(const QWeight &w, int64_t m, const void *x, void *out, int ot
   const auto *c = (const uint8_t *)w.codes;
   const auto *b = (const uint16_t *)w.biases;
   const auto *xx = (const uint16_t *)x;
-  if (kTripOk && w.k % 256 == 0)
+  if (g.gtab) {  // grouped rows (k % 32 == 0 checked by the caller for 4-bit codes)
+    if (kTripOk && w.k % 256 == 0)
+      hipLaunchKernelGGL((mfma_kernel<F, BM, BN, WGM, WGN, D, UK, true, ROT, SCHED, DX, kTripOk, true>), grid, block, 0,
+                         s, c, w.scales, b, w.global, xx, out, ot, m, w.n, w.k, tiles_m, tiles_n, g.gtab, g.gperm);
+    else if (vec)
+      hipLaunchKernelGGL((mfma_kernel<F, BM, BN, WGM, WGN, D, UK, true, ROT, SCHED, DX, false, true>), grid, block, 0,
+                         s, c, w.scales, b, w.global, xx, out, ot, m, w.n, w.k, tiles_m, tiles_n, g.gtab, g.gperm);
+    else
+      return hipErrorInvalidValue;
+  } else if (kTripOk && w.k % 256 == 0)
     hipLaunchKernelGGL((mfma_kernel<F, BM, BN, WGM, WGN, D, UK, true, ROT, SCHED, DX, kTripOk>), grid, block, 0, s, c,
-                       w.scales, b, w.global, xx, out, ot, m, w.n, w.k, tiles_m, tiles_n);
+                       w.scales, b, w.global, xx, out, ot, m, w.n, w.k, tiles_m, tiles_n, nullptr, 0);
   else if (vec)
     hipLaunchKernelGGL((mfma_kernel<F, BM, BN, WGM, WGN, D, UK, true, ROT, SCHED, DX, false>), grid, block, 0, s, c,
-                       w.scales, b, w.global, xx, out, ot, m, w.n, w.k, tiles_m, tiles_n);
+                       w.scales, b, w.global, xx, out, ot, m, w.n, w.k, tiles_m, tiles_n, nullptr, 0);
   else
     hipLaunchKernelGGL((mfma_kernel<F, BM, BN, WGM, WGN, D, UK, false, ROT, SCHED, DX, false>), grid, block, 0, s, c,
-                       w.scales, b, w.global, xx, out, ot, m, w.n, w.k, tiles_m, tiles_n);
+                       w.scales, b, w.global, xx, out, ot, m, w.n, w.k, tiles_m, tiles_n, nullptr, 0);
   return hipGetLastError();
 }
 
@@ -789,7 +823,34 @@ hipError_t run_f(const QWeight &w, int64_t m, const void *x, void *out, int ot, 
   return run_cfg<F, 128, 64, 2, 2, 2, 4, false, 4>(w, m, x, out, ot, s);
 }
 
+// Expert-grouped rows (the routing table from grouped.hip): 128-row tiles, so
+// tiles never straddle two experts' rows; 128x256 tiles with the step-ahead
+// schedule when the widest grid gives >= 128 tiles, else 128x64.
+template <int F>
+hipError_t run_grouped(const QWeight &w, int64_t m, const void *x, void *out, int ot, const int32_t *gtab,
+                       int64_t gperm, int tiles_m, hipStream_t s) {
+  const Grp g{gtab, gperm, tiles_m};
+  if ((int64_t)tiles_m * ((w.n + 63) / 64) > (int64_t)1 << 30) return hipErrorInvalidValue;
+  if (w.n >= 256 && (int64_t)tiles_m * ((w.n + 255) / 256) >= 128)
+    return run_cfg<F, 128, 256, 1, 8, 1, 4, false, 5>(w, m, x, out, ot, s, g);
+  return run_cfg<F, 128, 64, 2, 2, 2, 4, false, 4>(w, m, x, out, ot, s, g);
+}
+
 }  // namespace
+
+hipError_t launch_mfma_grouped(const QWeight &w, int64_t m, const void *x, void *out, int ot, const int32_t *gtab,
+                               int64_t gperm, int tiles_m, hipStream_t s) {
+  switch (w.fmt) {
+    case kMXFP4: return run_grouped<kMXFP4>(w, m, x, out, ot, gtab, gperm, tiles_m, s);
+    case kNVFP4: return run_grouped<kNVFP4>(w, m, x, out, ot, gtab, gperm, tiles_m, s);
+    case kMXFP8_E4M3: return run_grouped<kMXFP8_E4M3>(w, m, x, out, ot, gtab, gperm, tiles_m, s);
+    case kMXFP8_E5M2: return run_grouped<kMXFP8_E5M2>(w, m, x, out, ot, gtab, gperm, tiles_m, s);
+    case kNVFP8: return run_grouped<kNVFP8>(w, m, x, out, ot, gtab, gperm, tiles_m, s);
+    case kINT4_AFFINE: return run_grouped<kINT4_AFFINE>(w, m, x, out, ot, gtab, gperm, tiles_m, s);
+    case kINT8_SYM: return run_grouped<kINT8_SYM>(w, m, x, out, ot, gtab, gperm, tiles_m, s);
+  }
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_mfma(const QWeight &w, int64_t m, const void *x, void *out, int ot, hipStream_t s) {
   switch (w.fmt) {

@@ -17,6 +17,10 @@ The shapes follow the decode GEMV / prefill GEMM shapes of the pages (decode
 at n=k=4096, a 14336x4096 MLP projection with outliers, prefill at
 m=2048, n=k=4096, and an 11008x4096 projection at m=512); no public dataset
 is involved and no trained weights are needed.
+
+The expert-routed workload draws the stacked weights (step 1), then the
+routing (draw_expert_ids), then X (step 3) from its own stream; it stands in
+for a prefill-scale MoE layer's routed tokens.
 """
 from __future__ import annotations
 
@@ -56,6 +60,65 @@ WORKLOADS = {
         Workload("int8_sym_qgemm_512", "int8_sym", 512, 11008, 4096, 0.02, False, "bf16", 1004, "qgemm", 2e-3),
     ]
 }
+
+
+@dataclass(frozen=True)
+class MoeWorkload:
+    """A prefill-scale expert-routed matmul: `tokens` tokens, each routed to
+    `topk` distinct experts of `experts`, every expert an [n, k] weight packed
+    in one [experts*n, k] stack; m = tokens*topk routed rows (token-major)."""
+    name: str
+    fmt: str
+    tokens: int
+    topk: int
+    experts: int
+    n: int
+    k: int
+    sigma: float
+    seed: int
+    tol: float
+
+    @property
+    def m(self) -> int:
+        return self.tokens * self.topk
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.m * self.n * self.k
+
+
+MOE_WORKLOADS = {
+    w.name: w
+    for w in [
+        # 1024 tokens, top-2 of 8 experts of 4096 x 4096 (mxfp4): 2048 routed
+        # rows, the flops of the dense m=2048 prefill over 8x its weight bytes
+        MoeWorkload("mxfp4_moe_prefill_8x4096", "mxfp4", 1024, 2, 8, 4096, 4096, 0.02, 1006, 2e-3),
+    ]
+}
+
+
+def draw_expert_ids(tokens: int, topk: int, experts: int, rng) -> np.ndarray:
+    """Routed expert ids, int32 [tokens*topk] (token-major): per token, the
+    topk largest of experts standard-normal scores plus a per-expert offset
+    (drawn once, 0.5 * standard normal) that makes the expert loads uneven."""
+    bias = np.float32(0.5) * rng.standard_normal(experts, dtype=np.float32)
+    scores = rng.standard_normal((tokens, experts), dtype=np.float32) + bias
+    top = np.argsort(-scores, axis=1, kind="stable")[:, :topk]
+    return np.ascontiguousarray(top.reshape(-1), dtype=np.int32)
+
+
+def generate_moe(w: MoeWorkload | str, tokens: int | None = None):
+    """(W stack f32 [experts*n, k], X f32 [tokens*topk, k] bf16 values, ids)
+    for an expert-routed workload: weights, then ids, then activations from
+    one seeded stream."""
+    if isinstance(w, str):
+        w = MOE_WORKLOADS[w]
+    t = w.tokens if tokens is None else tokens
+    rng = np.random.default_rng(w.seed)
+    W = draw_weights(w.experts * w.n, w.k, w.sigma, False, rng)
+    ids = draw_expert_ids(t, w.topk, w.experts, rng)
+    X = draw_activations(t * w.topk, w.k, "bf16", rng)
+    return W, X, ids
 
 
 def draw_weights(n: int, k: int, sigma: float, outliers: bool, rng) -> np.ndarray:

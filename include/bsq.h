@@ -195,6 +195,30 @@ bsq_status bsq_gather_qmm(bsq_format fmt, int block, int64_t m, int64_t n, int64
                           const int32_t *expert_ids, const void *x, bsq_dtype xt, void *out, bsq_dtype ot,
                           int *status_dev, void *stream);
 
+/* Expert-grouped quantized matmul (prefill-scale MoE): the routed gather's
+ * result, out[i,j] = sum_p x[i,p] * dequant(W)[expert_ids[i]*n + j, p], over a
+ * stack of num_experts experts packed as ONE [num_experts*n, k] weight
+ * [metaltile PR #250, commit adding the per-token expert-routed qmm (the
+ * weight row is expert_ids[m]*out_dim + n); rlx-cpu quant.rs,
+ * lowp_scaled_grouped_matmul (the expert-indexed GEMM)], computed with the
+ * rows grouped by expert: a routing pass on the device sorts the rows by
+ * expert into a table in `workspace`, then the bf16 MFMA kernel runs 128-row
+ * tiles of each expert's rows, each expert's weight streamed once per tile
+ * instead of once per row.  x: device bf16 [m,k], 16-byte aligned (bf16 only:
+ * the MFMA path).  expert_ids: device int32 [m].  out: device [m,n] (ot).
+ * 1 <= num_experts <= 1024, m <= 2^24 (BSQ_ERR_SHAPE otherwise); 4-bit formats
+ * need k % 32 == 0 (BSQ_ERR_SHAPE).  workspace: device memory of at least
+ * bsq_grouped_qgemm_workspace(m, num_experts) bytes, 4-byte aligned, owned by
+ * the caller; its contents on entry do not matter and it must not be shared by
+ * calls in flight at the same time.  An id outside [0, num_experts) gives a
+ * zero output row and, if status_dev (device int, caller-initialised) is
+ * given, sets it to BSQ_ERR_ARG.  Asynchronous on stream. */
+bsq_status bsq_grouped_qgemm_workspace(int64_t m, int64_t num_experts, size_t *bytes);
+bsq_status bsq_grouped_qgemm(bsq_format fmt, int block, int64_t m, int64_t n, int64_t k, int64_t num_experts,
+                             const void *codes, const void *scales, const void *biases, float global_scale,
+                             const int32_t *expert_ids, const void *x, void *out, bsq_dtype ot, void *workspace,
+                             size_t workspace_bytes, int *status_dev, void *stream);
+
 /* Calibration (measurement only; not a step of the hot path).  A streaming
  * read of `bytes` bytes of the device buffer `buf` with the decode kernel's
  * load form (one 16-byte nontemporal load per lane, each byte read once,

@@ -141,6 +141,40 @@ def test_rmsnorm_qgemv_validation():
     assert f(bsq.MXFP4, 0, 0, 4, 64, q, q, None, 1.0, q, q, 1e-6, bsq.BF16, q, bsq.BF16, None) == bsq.OK  # m = 0
 
 
+def test_grouped_qgemm_workspace_and_validation():
+    """bsq_grouped_qgemm_workspace's size (1 + 3 per possible 128-row tile +
+    1 per row, in int32 words, the possible tiles being ceil(m/128) plus one
+    per expert that can hold rows) and the grouped call's checks before any
+    launch."""
+    import ctypes as C
+    W = bsq.bsq_grouped_qgemm_workspace
+    assert W(2048, 8) == (bsq.OK, 4 * (1 + 3 * (16 + 8) + 2048))
+    assert W(5, 1024) == (bsq.OK, 4 * (1 + 3 * (1 + 5) + 5))
+    assert W(0, 4) == (bsq.OK, 4)
+    assert W(10, 0)[0] == bsq.ERR_ARG and W(-1, 4)[0] == bsq.ERR_ARG
+    assert W(10, 1025)[0] == bsq.ERR_SHAPE and W((1 << 24) + 1, 4)[0] == bsq.ERR_SHAPE
+    q = C.c_void_p(256)  # never dereferenced: every call below returns before a launch
+    f = bsq.bsq_grouped_qgemm
+    ok_ws = 4 * (1 + 3 * (1 + 2) + 4)
+    assert f(bsq.MXFP4, 0, 4, 64, 48, 2, q, q, None, 1.0, q, q, q, bsq.BF16, q, ok_ws, None, None) == bsq.ERR_SHAPE
+    assert f(bsq.NVFP4, 0, 4, 64, 48, 2, q, q, None, 1.0, q, q, q, bsq.BF16, q, ok_ws, None, None) == bsq.ERR_SHAPE
+    assert f(bsq.MXFP4, 0, 4, 64, 64, 0, q, q, None, 1.0, q, q, q, bsq.BF16, q, ok_ws, None, None) == bsq.ERR_ARG
+    assert f(bsq.MXFP4, 0, 4, 64, 64, 1025, q, q, None, 1.0, q, q, q, bsq.BF16, q, ok_ws, None, None) == bsq.ERR_SHAPE
+    assert f(bsq.MXFP4, 0, 4, 64, 64, 2, q, q, None, 1.0, q, q, q, 7, q, ok_ws, None, None) == bsq.ERR_ARG
+    assert f(bsq.MXFP4, 0, 4, 64, 64, 2, q, q, None, 1.0, q, q, q, bsq.BF16, q, ok_ws - 4, None, None) == bsq.ERR_ARG
+    assert f(bsq.MXFP4, 0, 4, 64, 64, 2, q, q, None, 1.0, q, q, q, bsq.BF16, None, ok_ws, None, None) == bsq.ERR_ARG
+    assert f(bsq.MXFP4, 0, 4, 64, 64, 2, q, q, None, 1.0, None, q, q, bsq.BF16, q, ok_ws, None, None) == bsq.ERR_ARG
+    assert f(bsq.MXFP4, 0, 4, 64, 64, 2, q, q, None, 1.0, q, C.c_void_p(264), q, bsq.BF16, q, ok_ws, None,
+             None) == bsq.ERR_ALIGN
+    assert f(bsq.MXFP4, 0, 4, 64, 64, 2, q, q, None, 1.0, q, q, q, bsq.BF16, C.c_void_p(258), ok_ws, None,
+             None) == bsq.ERR_ALIGN
+    assert f(bsq.INT4_AFFINE, 0, 4, 64, 64, 2, q, q, None, 1.0, q, q, q, bsq.BF16, q, ok_ws, None, None) == bsq.ERR_ARG
+    assert f(bsq.MXFP4, 16, 4, 64, 64, 2, q, q, None, 1.0, q, q, q, bsq.BF16, q, ok_ws, None, None) == bsq.ERR_UNSUPPORTED
+    assert f(bsq.MXFP4, 0, 0, 64, 64, 2, q, q, None, 1.0, q, q, q, bsq.BF16, None, 0, None, None) == bsq.OK  # m = 0
+    assert f(bsq.MXFP4, 0, (1 << 24) + 1, 64, 64, 2, q, q, None, 1.0, q, q, q, bsq.BF16, q, ok_ws, None,
+             None) == bsq.ERR_SHAPE
+
+
 def test_bench_refuses_more_than_one_gpu():
     """The benchmark is one GPU's path: --gpus N > 1 exits with a message, before touching a device."""
     import subprocess
