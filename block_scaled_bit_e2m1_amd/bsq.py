@@ -33,7 +33,7 @@ OK, ERR_ARG, ERR_UNSUPPORTED, ERR_SHAPE, ERR_ALIGN, ERR_NONFINITE, ERR_HIP = 0, 
 
 EXPORTS = ["bsq_packed_bytes", "bsq_pack_host", "bsq_quantize", "bsq_dequant", "bsq_qgemv", "bsq_qgemm", "bsq_qgemm_path",
            "bsq_qgemm_mx", "bsq_rmsnorm_qgemv", "bsq_gather_qmm", "bsq_grouped_qgemm_workspace", "bsq_grouped_qgemm",
-           "bsq_calib_read", "bsq_calib_mfma",
+           "bsq_grouped_qgemm_noalloc", "bsq_calib_read", "bsq_calib_mfma",
            "bsq_status_string", "bsq_last_error", "bsq_version"]
 
 
@@ -69,11 +69,13 @@ def lib() -> ctypes.CDLL:
         L.bsq_grouped_qgemm_workspace.argtypes = [_i64, _i64, _sz]
         L.bsq_grouped_qgemm.argtypes = [_c_int, _c_int, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _f32, _vp, _vp, _vp,
                                         _c_int, _vp, ctypes.c_size_t, _vp, _vp]
+        L.bsq_grouped_qgemm_noalloc.argtypes = [_c_int, _c_int, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _f32, _vp, _vp,
+                                                _vp, _c_int, _vp, _vp]
         L.bsq_calib_read.argtypes = [_vp, _i64, _vp, _vp]
         L.bsq_calib_mfma.argtypes = [_i64, _i64, _vp, _vp]
         for f in ("bsq_packed_bytes", "bsq_pack_host", "bsq_quantize", "bsq_dequant", "bsq_qgemv", "bsq_qgemm", "bsq_qgemm_path",
                   "bsq_qgemm_mx", "bsq_rmsnorm_qgemv", "bsq_gather_qmm", "bsq_grouped_qgemm_workspace",
-                  "bsq_grouped_qgemm", "bsq_calib_read", "bsq_calib_mfma"):
+                  "bsq_grouped_qgemm", "bsq_grouped_qgemm_noalloc", "bsq_calib_read", "bsq_calib_mfma"):
             getattr(L, f).restype = _c_int
         for f in ("bsq_status_string", "bsq_last_error", "bsq_version"):
             getattr(L, f).restype = ctypes.c_char_p
@@ -137,6 +139,12 @@ def bsq_grouped_qgemm(fmt, block, m, n, k, num_experts, codes, scales, biases, g
                       workspace, workspace_bytes, status_dev, stream):
     return lib().bsq_grouped_qgemm(fmt, block, m, n, k, num_experts, codes, scales, biases, global_scale, expert_ids,
                                    x, out, ot, workspace, workspace_bytes, status_dev, stream)
+
+
+def bsq_grouped_qgemm_noalloc(fmt, block, m, n, k, num_experts, codes, scales, biases, global_scale, expert_ids, x,
+                              out, ot, status_dev, stream):
+    return lib().bsq_grouped_qgemm_noalloc(fmt, block, m, n, k, num_experts, codes, scales, biases, global_scale,
+                                           expert_ids, x, out, ot, status_dev, stream)
 
 
 def bsq_calib_read(buf, nbytes, sink, stream):

@@ -258,10 +258,14 @@ bsq_status bsq_grouped_qgemm_workspace(int64_t m, int64_t num_experts, size_t *b
   return ok();
 }
 
-bsq_status bsq_grouped_qgemm(bsq_format fmt, int block, int64_t m, int64_t n, int64_t k, int64_t num_experts,
-                             const void *codes, const void *scales, const void *biases, float global_scale,
-                             const int32_t *expert_ids, const void *x, void *out, bsq_dtype ot, void *workspace,
-                             size_t workspace_bytes, int *status_dev, void *stream) {
+namespace {
+
+// The grouped call's checks and launch; workspace == nullptr && noalloc takes
+// the routing table from the library's own device array instead.
+bsq_status grouped(bsq_format fmt, int block, int64_t m, int64_t n, int64_t k, int64_t num_experts, const void *codes,
+                   const void *scales, const void *biases, float global_scale, const int32_t *expert_ids,
+                   const void *x, void *out, bsq_dtype ot, void *workspace, size_t workspace_bytes, bool noalloc,
+                   int *status_dev, void *stream) {
   bsq_status s;
   if ((s = check_format(fmt, block))) return s;
   if (num_experts < 1) return fail(BSQ_ERR_ARG, "num_experts must be >= 1");
@@ -272,6 +276,10 @@ bsq_status bsq_grouped_qgemm(bsq_format fmt, int block, int64_t m, int64_t n, in
   if (m > ((int64_t)1 << 24)) return fail(BSQ_ERR_SHAPE, "m=%lld: at most 2^24 rows", (long long)m);
   if (ot != BSQ_F32 && ot != BSQ_BF16) return fail(BSQ_ERR_ARG, "bad out dtype %d", (int)ot);
   if (bsq::is_4bit(fmt) && k % 32) return fail(BSQ_ERR_SHAPE, "k=%lld: 4-bit formats need k %% 32 == 0 here", (long long)k);
+  const int64_t need = bsq::grouped_workspace_bytes(m, num_experts);
+  if (noalloc && need > bsq::kNoAllocTableBytes)
+    return fail(BSQ_ERR_SHAPE, "m=%lld, %lld experts: the routing table needs %lld bytes, the built-in one holds %lld",
+                (long long)m, (long long)num_experts, (long long)need, (long long)bsq::kNoAllocTableBytes);
   if (m == 0 || n == 0) return ok();
   if (!out) return fail(BSQ_ERR_ARG, "null out");
   if (!aligned(out, ot == BSQ_F32 ? 4 : 2)) return fail(BSQ_ERR_ALIGN, "out misaligned");
@@ -282,13 +290,35 @@ bsq_status bsq_grouped_qgemm(bsq_format fmt, int block, int64_t m, int64_t n, in
   if (!aligned(x, 16) || !aligned(expert_ids, 4)) return fail(BSQ_ERR_ALIGN, "x (16) or expert_ids (4) misaligned");
   if (status_dev && !aligned(status_dev, 4)) return fail(BSQ_ERR_ALIGN, "status misaligned");
   if (m > ((int64_t)1 << 40) / k) return fail(BSQ_ERR_SHAPE, "m*k too large");
-  const int64_t need = bsq::grouped_workspace_bytes(m, num_experts);
-  if (!workspace || (int64_t)workspace_bytes < need)
-    return fail(BSQ_ERR_ARG, "workspace of %lld bytes needed", (long long)need);
-  if (!aligned(workspace, 4)) return fail(BSQ_ERR_ALIGN, "workspace must be 4-byte aligned");
+  if (noalloc) {
+    hipError_t e = bsq::grouped_scratch(&workspace);
+    if (e != hipSuccess) return hip_status(e, "routing table lookup");
+  } else {
+    if (!workspace || (int64_t)workspace_bytes < need)
+      return fail(BSQ_ERR_ARG, "workspace of %lld bytes needed", (long long)need);
+    if (!aligned(workspace, 4)) return fail(BSQ_ERR_ALIGN, "workspace must be 4-byte aligned");
+  }
   const bsq::QWeight w{(int)fmt, n, k, codes, scales, biases, global_scale};
   return hip_status(bsq::launch_grouped(w, m, num_experts, expert_ids, x, out, (int)ot, workspace, status_dev, st),
                     "grouped launch");
+}
+
+}  // namespace
+
+bsq_status bsq_grouped_qgemm(bsq_format fmt, int block, int64_t m, int64_t n, int64_t k, int64_t num_experts,
+                             const void *codes, const void *scales, const void *biases, float global_scale,
+                             const int32_t *expert_ids, const void *x, void *out, bsq_dtype ot, void *workspace,
+                             size_t workspace_bytes, int *status_dev, void *stream) {
+  return grouped(fmt, block, m, n, k, num_experts, codes, scales, biases, global_scale, expert_ids, x, out, ot,
+                 workspace, workspace_bytes, false, status_dev, stream);
+}
+
+bsq_status bsq_grouped_qgemm_noalloc(bsq_format fmt, int block, int64_t m, int64_t n, int64_t k, int64_t num_experts,
+                                     const void *codes, const void *scales, const void *biases, float global_scale,
+                                     const int32_t *expert_ids, const void *x, void *out, bsq_dtype ot,
+                                     int *status_dev, void *stream) {
+  return grouped(fmt, block, m, n, k, num_experts, codes, scales, biases, global_scale, expert_ids, x, out, ot,
+                 nullptr, 0, true, status_dev, stream);
 }
 
 bsq_status bsq_calib_read(const void *buf, int64_t bytes, float *sink, void *stream) {

@@ -84,6 +84,12 @@ hipError_t launch_mxmma(int xfmt, const void *xc, const void *xs, int wfmt, cons
 // grouped_workspace_bytes(m, E) bytes holds the routing table.
 constexpr int kMaxExperts = 1024;
 int64_t grouped_workspace_bytes(int64_t m, int64_t nexp);
+// The routing table of the allocation-free grouped call: a file-scope device
+// array of this many bytes in grouped.hip; grouped_scratch gives its address
+// on the current device (looked up once per device).
+constexpr int64_t kNoAllocTableBytes = (int64_t)1 << 20;
+constexpr int kMaxDevices = 64;
+hipError_t grouped_scratch(void **ptr);
 hipError_t launch_grouped(const QWeight &w, int64_t m, int64_t nexp, const int32_t *eids, const void *x, void *out,
                           int ot, void *workspace, int *status, hipStream_t s);
 // The grouped form of the MFMA kernel (mfma.hip) over a routing table: gtab[0]

@@ -18,6 +18,8 @@
 // The order of rows inside an expert's group comes from LDS atomics, but every
 // output row is computed the same way wherever it sits, so the result is
 // bit-for-bit the same from run to run.
+#include <mutex>
+
 #include "bsq_internal.hpp"
 
 namespace bsq {
@@ -111,6 +113,38 @@ int64_t perm_offset(int64_t m, int64_t nexp) { return 1 + 3 * max_tiles(m, nexp)
 int64_t table_words(int64_t m, int64_t nexp) { return perm_offset(m, nexp) + m; }
 
 }  // namespace
+
+// ---- the routing table of the allocation-free call ----
+//
+// A file-scope device array, one per device the library runs on, held until
+// the process ends.  Its host-side name is not a device address: its address
+// on each device is looked up once, with that device current, and only that
+// address is handed to kernels.  Every allocation-free call on a device
+// shares the device's table, so such calls that overlap on one device race.
+// Nothing in it needs to start at zero: the route kernel writes every word a
+// call then reads (tile count, tile entries, sorted rows) before the GEMM.
+static __device__ __align__(256) int32_t scratch[kNoAllocTableBytes / 4];
+
+namespace {
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t grouped_scratch(void **ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 int64_t grouped_workspace_bytes(int64_t m, int64_t nexp) { return 4 * table_words(m, nexp); }
 

@@ -219,6 +219,21 @@ bsq_status bsq_grouped_qgemm(bsq_format fmt, int block, int64_t m, int64_t n, in
                              const int32_t *expert_ids, const void *x, void *out, bsq_dtype ot, void *workspace,
                              size_t workspace_bytes, int *status_dev, void *stream);
 
+/* bsq_grouped_qgemm without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, result, checks and errors as bsq_grouped_qgemm; the routing
+ * table lives in a 1 MiB array the library keeps on each device until the
+ * process ends, so m and num_experts must satisfy
+ * bsq_grouped_qgemm_workspace(m, num_experts) <= 1 MiB (any m <= 253000 fits,
+ * whatever num_experts; BSQ_ERR_SHAPE otherwise).  Calls on one device share
+ * that array: two such calls in flight at once on one device (on different
+ * streams, or from different threads) race and give wrong results. */
+bsq_status bsq_grouped_qgemm_noalloc(bsq_format fmt, int block, int64_t m, int64_t n, int64_t k, int64_t num_experts,
+                                     const void *codes, const void *scales, const void *biases, float global_scale,
+                                     const int32_t *expert_ids, const void *x, void *out, bsq_dtype ot,
+                                     int *status_dev, void *stream);
+
 /* Calibration (measurement only; not a step of the hot path).  A streaming
  * read of `bytes` bytes of the device buffer `buf` with the decode kernel's
  * load form (one 16-byte nontemporal load per lane, each byte read once,
