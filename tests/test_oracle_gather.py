@@ -21,6 +21,24 @@ def test_single_expert_is_the_plain_matmul():
     assert (ref == r2).all() and (den == d2).all()
 
 
+def test_grouped_rows_equal_each_experts_plain_matmul():
+    """Grouping the rows by expert (the schedule of the grouped GEMM) gives,
+    for every expert e, the plain matmul of e's rows with e's slice of the
+    stack; the experts with no rows contribute nothing."""
+    rng = np.random.default_rng(3)
+    E, n, k, m = 6, 5, 64, 40
+    wd = rng.standard_normal((E * n, k)).astype(np.float32)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    ids = rng.choice([0, 2, 3, 5], m).astype(np.int32)  # experts 1 and 4 get no rows
+    ref, den = oracle.gather_matmul(x, wd, ids, n)
+    for e in range(E):
+        rows = np.flatnonzero(ids == e)
+        if rows.size == 0:
+            continue
+        r2, d2 = oracle.matmul(x[rows], wd[e * n:(e + 1) * n])
+        assert (ref[rows] == r2).all() and (den[rows] == d2).all()
+
+
 def test_constant_experts_closed_form():
     """Expert e is the constant matrix (e + 1): row i's output is
     (ids[i] + 1) * sum(x[i]) in every column."""
