@@ -51,7 +51,10 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* The enumerated arguments and results are plain ints (the enumerators name
+ * the accepted values): a value outside a list reaches the library as an
+ * ordinary int and is rejected with a status, never read as an invalid enum. */
+enum {
     BSQ_OK = 0,
     BSQ_ERR_ARG = 1,         /* null pointer, negative size, bad dtype */
     BSQ_ERR_UNSUPPORTED = 2, /* unknown format, or block != the format's block */
@@ -59,9 +62,10 @@ typedef enum {
     BSQ_ERR_ALIGN = 4,       /* pointer misaligned for the kernel's vector loads */
     BSQ_ERR_NONFINITE = 5,   /* pack input holds NaN or inf */
     BSQ_ERR_HIP = 6          /* HIP launch / runtime error (see bsq_last_error) */
-} bsq_status;
+};
+typedef int bsq_status;
 
-typedef enum {
+enum {
     BSQ_MXFP4 = 1,
     BSQ_NVFP4 = 2,
     BSQ_MXFP8_E4M3 = 3,
@@ -69,16 +73,19 @@ typedef enum {
     BSQ_NVFP8 = 5,
     BSQ_INT4_AFFINE = 6,
     BSQ_INT8_SYM = 7
-} bsq_format;
+};
+typedef int bsq_format;
 
-typedef enum { BSQ_F32 = 0, BSQ_BF16 = 1 } bsq_dtype;
+enum { BSQ_F32 = 0, BSQ_BF16 = 1 };
+typedef int bsq_dtype;
 
 /* Kernel family selector for bsq_qgemm_path. */
-typedef enum {
+enum {
     BSQ_PATH_AUTO = 0,  /* library choice by shape and dtype */
     BSQ_PATH_ROWS = 1,  /* VALU streaming kernel: W decoded once, FMA against every X row */
     BSQ_PATH_MFMA = 2   /* LDS-tiled bf16 MFMA kernel (bf16 X only) */
-} bsq_path;
+};
+typedef int bsq_path;
 
 /* Byte sizes of the packed representation of an [n,k] weight
  * ("byte-layout sizes" [metaltile PR #250, format tests]).  `block` is 0 for

@@ -143,6 +143,32 @@ def test_dequant_integer_and_f32_scale_sweeps():
     assert same_bits(bsq.dequant(d).cpu().numpy(), oracle.dequant_packed(p)).all()
 
 
+# ----------------------------------------------------------------- guard bands
+GUARD = 256  # elements of canary before and after every guarded output
+
+
+def _canary(size, dtype):
+    """3 + 0.25 * (i mod 127): distinct neighbours, exact in bf16 and f32."""
+    return torch.arange(size, device=DEV).remainder(127).to(torch.float32).mul_(0.25).add_(3.0).to(dtype)
+
+
+def guarded(shape, dtype):
+    """An output of `shape` inside one buffer with GUARD canary elements
+    before and after it (the output stays 16-byte aligned)."""
+    size = int(np.prod(shape))
+    buf = torch.empty(size + 2 * GUARD, dtype=dtype, device=DEV)
+    buf.copy_(_canary(buf.numel(), dtype))
+    return buf, buf[GUARD:GUARD + size].view(shape)
+
+
+def check_guard(buf, size, what=""):
+    """The canary bands around a guarded output are untouched."""
+    torch.cuda.synchronize()
+    want = _canary(buf.numel(), buf.dtype)
+    lo, hi = slice(0, GUARD), slice(GUARD + size, buf.numel())
+    assert torch.equal(buf[lo], want[lo]) and torch.equal(buf[hi], want[hi]), f"{what}: write outside the output"
+
+
 # ----------------------------------------------------------------- matmul
 def run_matmul(fmt, m, n, k, act, path, seed=0, sigma=0.02, outliers=True, out_dtype=None):
     W = workloads.random_weights(n, k, seed=seed + 17, sigma=sigma, outliers=outliers)
@@ -152,10 +178,12 @@ def run_matmul(fmt, m, n, k, act, path, seed=0, sigma=0.02, outliers=True, out_d
     ref, den = oracle.matmul(X, wd)
     xt = torch.from_numpy(X).to(torch.bfloat16 if act == "bf16" else torch.float32).to(DEV)
     od = out_dtype or xt.dtype
+    buf, out = guarded((m, n), od)
     if path == "gemv":
-        out = bsq.qgemv(d, xt[0], out_dtype=od)[None, :]
+        bsq.qgemv(d, xt[0], out=out[0])
     else:
-        out = bsq.qgemm(d, xt, out_dtype=od, path=path)
+        bsq.qgemm(d, xt, out=out, path=path)
+    check_guard(buf, m * n, f"{fmt} m={m} n={n} k={k} path={path}")
     return out.float().cpu().numpy(), ref, den, od == torch.bfloat16
 
 
@@ -217,7 +245,10 @@ def test_qgemm_mfma_wide_tiles(fmt):
         X = workloads.random_activations(m, k, seed=m + k + 1)
         p, d = packed(fmt, W)
         xt = torch.from_numpy(X).to(torch.bfloat16).to(DEV)
-        out = bsq.qgemm(d, xt, out_dtype=od, path=bsq.PATH_MFMA).float().cpu().numpy()
+        buf, o = guarded((m, n), od)
+        bsq.qgemm(d, xt, out=o, path=bsq.PATH_MFMA)
+        check_guard(buf, m * n, f"mfma wide {fmt} m={m} n={n} k={k}")
+        out = o.float().cpu().numpy()
         rows = np.unique(np.concatenate([[0, 127, 128, 255, m - 1], rng.choice(m, 27, replace=False)]))
         ref, den = oracle.matmul(X, oracle.dequant_packed(p), rows=rows)
         check_bound(out[rows], ref, den, 2e-3, f"mfma wide {fmt} m={m} n={n} k={k}", od == torch.bfloat16)
@@ -430,7 +461,10 @@ def _mx_case(xfmt, wfmt, m, n, k, seed, out_dtype, rows=None):
     pw = oracle.pack(wfmt, W)
     wd = bsq.to_device(bsq.PackedWeight(pw["fmt"], n, k, torch.from_numpy(pw["codes"]), torch.from_numpy(pw["scales"]),
                                         None, 1.0), DEV)
-    out = bsq.qgemm_mx(xq, wd, out_dtype=out_dtype).float().cpu().numpy()
+    buf, o = guarded((m, n), out_dtype)
+    bsq.qgemm_mx(xq, wd, out=o)
+    check_guard(buf, m * n, f"qgemm_mx {xfmt} x {wfmt} m={m} n={n} k={k}")
+    out = o.float().cpu().numpy()
     xd = oracle.dequant_packed(px)
     if rows is not None:
         out = out[rows]
@@ -529,8 +563,10 @@ def _rmsnorm_case(fmt, m, n, k, act, eps, seed, out_dtype=None):
     tdt = torch.bfloat16 if act == "bf16" else torch.float32
     x = torch.from_numpy(X).to(tdt).to(DEV)
     gt = torch.from_numpy(g).to(tdt).to(DEV)
-    out = bsq.rmsnorm_qgemv(pw, x, gt, eps, out_dtype=out_dtype).float().cpu().numpy()
-    return out, ref, den
+    buf, o = guarded((m, n), out_dtype or tdt)
+    bsq.rmsnorm_qgemv(pw, x, gt, eps, out=o)
+    check_guard(buf, m * n, f"rmsnorm_qgemv {fmt} m={m} n={n} k={k}")
+    return o.float().cpu().numpy(), ref, den
 
 
 @pytest.mark.parametrize("fmt", ALL)
@@ -583,8 +619,10 @@ def _gather_case(fmt, E, n, k, ids, act, seed):
     x = torch.from_numpy(X).to(tdt).to(DEV)
     eids = torch.tensor(ids, dtype=torch.int32, device=DEV)
     status = torch.zeros(1, dtype=torch.int32, device=DEV)
-    out = bsq.gather_qmm(stack, E, eids, x, status=status).float().cpu().numpy()
-    return out, ref, den, int(status.item())
+    buf, o = guarded((len(ids), n), tdt)
+    bsq.gather_qmm(stack, E, eids, x, out=o, status=status)
+    check_guard(buf, len(ids) * n, f"gather_qmm {fmt} E={E} n={n} k={k}")
+    return o.float().cpu().numpy(), ref, den, int(status.item())
 
 
 @pytest.mark.parametrize("fmt", ALL)
