@@ -64,6 +64,11 @@ hipError_t launch_rows_gather(const QWeight &w, int64_t m, const void *x, int xt
 bool gemv_applies(const QWeight &w, int64_t m, int xt, bool routed);
 hipError_t launch_gemv(const QWeight &w, int64_t m, const void *x, void *out, int ot, const int32_t *eids,
                        int64_t nexp, int *status, hipStream_t s);
+// The fused RMSNorm on the decode GEMV kernel: one bf16 row, k = 64 chunks per
+// wave of the k split (4096 for every format).
+bool gemv_norm_applies(const QWeight &w, int64_t m, int xt);
+hipError_t launch_gemv_norm(const QWeight &w, const void *x, const void *gam, float eps, void *out, int ot,
+                            hipStream_t s);
 // MFMA kernel: bf16 X, any m >= 1.
 hipError_t launch_mfma(const QWeight &w, int64_t m, const void *x, void *out, int ot, hipStream_t s);
 // Zero-fill an output of `bytes` bytes (k == 0 case).

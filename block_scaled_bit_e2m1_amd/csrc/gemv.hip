@@ -158,6 +158,37 @@ __device__ __forceinline__ float chunk_dot(v4u c, uint32_t s, uint32_t b, const 
   }
 }
 
+// chunk_dot against f32 activations (the fused RMSNorm's x * g, exact in f32).
+template <int F>
+__device__ __forceinline__ float chunk_dot_f32(v4u c, uint32_t s, uint32_t b, const float (&xf)[kE<F>], float acc) {
+  if constexpr (F == kNVFP4) {
+    float p0 = dot8_f32<F>(c.x, 0u, xf + 0, 0.0f);
+    p0 = dot8_f32<F>(c.y, 0u, xf + 8, p0);
+    float p1 = dot8_f32<F>(c.z, 0u, xf + 16, 0.0f);
+    p1 = dot8_f32<F>(c.w, 0u, xf + 24, p1);
+    const f32x2_t sv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(s, 1.0f, false);
+    acc = __builtin_fmaf(p0, sv[0], acc);
+    return __builtin_fmaf(p1, sv[1], acc);
+  } else if constexpr (Traits<F>::kBits == 4) {
+    float p = dot8_f32<F>(c.x, 0u, xf + 0, 0.0f);
+    p = dot8_f32<F>(c.y, 0u, xf + 8, p);
+    p = dot8_f32<F>(c.z, 0u, xf + 16, p);
+    p = dot8_f32<F>(c.w, 0u, xf + 24, p);
+    acc = __builtin_fmaf(p, block_scale<F>(s), acc);
+    if constexpr (F == kINT4_AFFINE) {
+      float xs = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) xs += xf[i];
+      acc = __builtin_fmaf(xs, bf16_bits_to_f32(b), acc);
+    }
+    return acc;
+  } else {
+    float p = dot8_f32<F>(c.x, c.y, xf + 0, 0.0f);
+    p = dot8_f32<F>(c.z, c.w, xf + 8, p);
+    return __builtin_fmaf(p, block_scale<F>(s), acc);
+  }
+}
+
 // Launch parameters, with the per-row byte counts and the chunk count worked
 // out on the host (the kernel does no division by a runtime value).
 struct GemvParams {
@@ -174,6 +205,8 @@ struct GemvParams {
   float global;
   int ot;              // 0: f32 out, 1: bf16 out
   int C;               // 16-byte code chunks per row
+  const uint16_t *g;   // fused RMSNorm: the norm weight (bf16 [k]), and its eps
+  float eps;
 };
 
 // O32: every code and scale byte offset of the (stacked) weight fits in 31
@@ -345,7 +378,12 @@ __global__ void __launch_bounds__(WPG * 64) gemv_kernel(const GemvParams p) {
 // faster than the general kernel with its single round selected at compile
 // time (nvfp4 4096 x 4096: 3.65 vs 3.9 us; the set-up of the general kernel,
 // scalar row offsets and scalar-base loads, costs the difference).
-template <int F, int KW, int R, int S, int WPG>
+// NORM: the fused RMSNorm (one bf16 row): each lane also loads its chunk of
+// the norm weight g, multiplies x * g in f32 (exact for bf16 inputs) and sums
+// x^2; the dots run against x * g in f32, and the row's 1 / sqrt(mean x^2 +
+// eps) scales each output once, after the sums of x^2 of the k-split waves
+// meet in LDS with the dots.
+template <int F, int KW, int R, int S, int WPG, bool NORM = false>
 __global__ void __launch_bounds__(WPG * 64) gemv1_kernel(const GemvParams p) {
   constexpr int E = kE<F>, XQ = E / 8, RG = WPG / KW, RS = R * S;
   constexpr int SB = (F == kNVFP8 || F == kINT8_SYM) ? 4 : (F == kINT4_AFFINE ? 2 : 1);
@@ -364,10 +402,11 @@ __global__ void __launch_bounds__(WPG * 64) gemv1_kernel(const GemvParams p) {
     if (skip && p.status && blockIdx.x == 0 && threadIdx.x == 0) *p.status = 1;
     jbase = skip ? 0 : e * n;
   }
-  __shared__ float red[KW > 1 ? WPG : 1][RS];
+  __shared__ float red[KW > 1 ? WPG : 1][RS + (NORM ? 1 : 0)];
   v4u cw[S][R];
   uint32_t sw[S][R], bw[S][R];
   uint4 xq[XQ];
+  uint4 gq[NORM ? XQ : 1];
   float acc[S][R];
   auto load_group = [&](int s) {
 #pragma unroll
@@ -384,10 +423,31 @@ __global__ void __launch_bounds__(WPG * 64) gemv1_kernel(const GemvParams p) {
     const uint16_t *xr = p.x + (size_t)i * (size_t)p.k;
 #pragma unroll
     for (int q = 0; q < XQ; ++q) xq[q] = reinterpret_cast<const uint4 *>(xr + ch * E)[q];
+    if constexpr (NORM) {
+#pragma unroll
+      for (int q = 0; q < XQ; ++q) gq[q] = reinterpret_cast<const uint4 *>(p.g + ch * E)[q];
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 1; s < S; ++s) load_group(s);
     __builtin_amdgcn_sched_barrier(0);
+  }
+  // NORM: x * g and this lane's share of sum x^2
+  float xg[NORM ? E : 1];
+  float ssq = 0.0f;
+  if constexpr (NORM) {
+#pragma unroll
+    for (int q = 0; q < XQ; ++q) {
+      const uint32_t xv[4] = {xq[q].x, xq[q].y, xq[q].z, xq[q].w}, gv[4] = {gq[q].x, gq[q].y, gq[q].z, gq[q].w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float x0 = __uint_as_float(xv[t] << 16), x1 = __uint_as_float(xv[t] & 0xFFFF0000u);
+        xg[8 * q + 2 * t] = x0 * __uint_as_float(gv[t] << 16);
+        xg[8 * q + 2 * t + 1] = x1 * __uint_as_float(gv[t] & 0xFFFF0000u);
+        ssq = __builtin_fmaf(x0, x0, ssq);
+        ssq = __builtin_fmaf(x1, x1, ssq);
+      }
+    }
   }
   auto store = [&](int j, float v) {
     if constexpr (F == kNVFP4) v *= p.global;
@@ -402,7 +462,8 @@ __global__ void __launch_bounds__(WPG * 64) gemv1_kernel(const GemvParams p) {
       acc[s][r] = 0.0f;
       if (!skip) {
         asm volatile("" : "+v"(cw[s][r]), "+v"(sw[s][r]));
-        acc[s][r] = chunk_dot<F>(cw[s][r], sw[s][r], bw[s][r], xq, 0.0f);
+        if constexpr (NORM) acc[s][r] = chunk_dot_f32<F>(cw[s][r], sw[s][r], bw[s][r], xg, 0.0f);
+        else acc[s][r] = chunk_dot<F>(cw[s][r], sw[s][r], bw[s][r], xq, 0.0f);
       }
     }
     const float v = joint_sum<R>(acc[s]);
@@ -417,12 +478,23 @@ __global__ void __launch_bounds__(WPG * 64) gemv1_kernel(const GemvParams p) {
       }
     }
   }
+  static_assert(!NORM || KW > 1, "the fused norm's sums meet in the k-split reduction");
+  if constexpr (NORM) {
+    const float tq = wave_sum(ssq);
+    if (lane == 0) red[w][RS] = tq;
+  }
   if constexpr (KW > 1) {
     __syncthreads();
     if (ks == 0 && lane < RS && j0 + lane < n) {
       float t = 0.0f;
 #pragma unroll
       for (int q = 0; q < KW; ++q) t += red[rg * KW + q][lane];
+      if constexpr (NORM) {
+        float sq = 0.0f;
+#pragma unroll
+        for (int q = 0; q < KW; ++q) sq += red[rg * KW + q][RS];
+        t *= 1.0f / sqrtf(sq / (float)p.k + p.eps);
+      }
       store(j0 + lane, t);
     }
   }
@@ -435,7 +507,7 @@ __global__ void __launch_bounds__(WPG * 64) gemv1_kernel(const GemvParams p) {
 // (mxfp8 14336 x 4096: 10.7 us against a 10.1 us pure read of the codes).
 template <int F>
 hipError_t run(const QWeight &w, int64_t m, const void *x, void *out, int ot, const int32_t *eids, int64_t nexp,
-               int *status, hipStream_t s) {
+               int *status, hipStream_t s, const void *gam = nullptr, float eps = 0.0f) {
   constexpr bool k4 = Traits<F>::kBits == 4;
   constexpr int KW = k4 ? 2 : 4, R = 2, S = k4 ? 2 : 1, WPG = k4 ? 8 : 4;
   constexpr int rows_per_wg = (WPG / KW) * R * S;
@@ -459,11 +531,18 @@ hipError_t run(const QWeight &w, int64_t m, const void *x, void *out, int ot, co
   p.global = w.global;
   p.ot = ot;
   p.C = (int)(w.k / (k4 ? 32 : 16));
+  p.g = (const uint16_t *)gam;
+  p.eps = eps;
   const int64_t total_rows = w.n * (eids ? nexp : 1);
   // 32-bit offsets: the codes (scales are smaller) and the activation rows
   const bool o32 = total_rows * (int64_t)p.rowb < ((int64_t)1 << 31) && m * w.k < ((int64_t)1 << 30);
   const bool one = p.C == 64 * KW;
   const dim3 grid((unsigned)wgs, (unsigned)m), block(WPG * 64);
+  if (gam) {  // the fused RMSNorm: the one-round kernel only (checked by gemv_norm_applies)
+    if (!(o32 && one) || m != 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemv1_kernel<F, KW, R, S, WPG, true>), grid, block, 0, s, p);
+    return hipGetLastError();
+  }
   if (o32 && one) hipLaunchKernelGGL((gemv1_kernel<F, KW, R, S, WPG>), grid, block, 0, s, p);
   else if (o32) hipLaunchKernelGGL((gemv_kernel<F, KW, R, S, WPG, true, false>), grid, block, 0, s, p);
   else hipLaunchKernelGGL((gemv_kernel<F, KW, R, S, WPG, false, false>), grid, block, 0, s, p);
@@ -476,6 +555,27 @@ bool gemv_applies(const QWeight &w, int64_t m, int xt, bool routed) {
   // bf16 activations, whole 16-byte code chunks, one weight pass per row
   const int64_t E = is_4bit(w.fmt) ? 32 : 16;
   return xt == 1 && w.k % E == 0 && w.k / E < ((int64_t)1 << 30) && (m == 1 || routed);
+}
+
+bool gemv_norm_applies(const QWeight &w, int64_t m, int xt) {
+  // one bf16 row, one full round of 16-byte chunks per wave (k = 4096), 31-bit offsets
+  const bool k4 = is_4bit(w.fmt);
+  const int64_t E = k4 ? 32 : 16, KW = k4 ? 2 : 4;
+  return xt == 1 && m == 1 && w.k == 64 * KW * E && w.n * (k4 ? w.k / 2 : w.k) < ((int64_t)1 << 31);
+}
+
+hipError_t launch_gemv_norm(const QWeight &w, const void *x, const void *gam, float eps, void *out, int ot,
+                            hipStream_t s) {
+  switch (w.fmt) {
+    case kMXFP4: return run<kMXFP4>(w, 1, x, out, ot, nullptr, 0, nullptr, s, gam, eps);
+    case kNVFP4: return run<kNVFP4>(w, 1, x, out, ot, nullptr, 0, nullptr, s, gam, eps);
+    case kMXFP8_E4M3: return run<kMXFP8_E4M3>(w, 1, x, out, ot, nullptr, 0, nullptr, s, gam, eps);
+    case kMXFP8_E5M2: return run<kMXFP8_E5M2>(w, 1, x, out, ot, nullptr, 0, nullptr, s, gam, eps);
+    case kNVFP8: return run<kNVFP8>(w, 1, x, out, ot, nullptr, 0, nullptr, s, gam, eps);
+    case kINT4_AFFINE: return run<kINT4_AFFINE>(w, 1, x, out, ot, nullptr, 0, nullptr, s, gam, eps);
+    case kINT8_SYM: return run<kINT8_SYM>(w, 1, x, out, ot, nullptr, 0, nullptr, s, gam, eps);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemv(const QWeight &w, int64_t m, const void *x, void *out, int ot, const int32_t *eids,
