@@ -688,31 +688,31 @@ mfma_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ scales, 
 
     // prologue: steps 0 and 1 in LDS, step 2's X in its slot, step 0's
     // weights decoded, steps 1..D's weights in flight
-    loadx(kGuarded, gx[0], 0);
-    storex(gx[0], 0);
-    if (KT > 1) {
-      loadx(kGuarded, gx[0], 1);
-      storex(gx[0], 1);
-    }
-#pragma unroll
-    for (int q = 2; q < 2 + DX; ++q)
-      if (q < KT) loadx(kGuarded, gx[q % DX], q);
-    if constexpr (kTS) {
-      loadsc(tsc, 0);
-      if (NTRIP > 1) loadsc(tsn, 1);
-    }
+    // every prologue load is issued before the first one is waited for
     {
+      SX x1;
       WRaw w0[NT];
+      loadx(kGuarded, gx[0], 0);
+      if (KT > 1) loadx(kGuarded, x1, 1);
+      if constexpr (kTS) {
+        loadsc(tsc, 0);
+        if (NTRIP > 1) loadsc(tsn, 1);
+      }
       loadw(kGuarded, w0, 0);
+#pragma unroll
+      for (int q = 1; q <= D; ++q)
+        if (q < KT) loadw(kGuarded, gw[q % D], q);
+      storex(gx[0], 0);
+      if (KT > 1) storex(x1, 1);
+#pragma unroll
+      for (int q = 2; q < 2 + DX; ++q)
+        if (q < KT) loadx(kGuarded, gx[q % DX], q);
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
         if constexpr (kTS) trip_sc<F, 0, FOLD>(w0[j], tsc[j], h);
         decode_w<F, FOLD>(w0[j], bh[j], bl[j], fs[j]);
       }
     }
-#pragma unroll
-    for (int q = 1; q <= D; ++q)
-      if (q < KT) loadw(kGuarded, gw[q % D], q);
     __syncthreads();
     read_a(xs[0], 0, a0);
 

@@ -19,19 +19,22 @@
 // a 4-bit lane reads chunk 2h+s, an 8-bit lane chunks h+2s and 4+h+2s.
 //
 // Data movement.  Partial-line global loads leave the kernel bound by L1
-// accesses, so every global load reads whole contiguous runs: both code tiles
-// go through LDS (consecutive threads on consecutive 16-byte chunks of a row),
-// written with the chunk index XOR-swizzled by row so that the row writes and
-// the per-lane operand reads are both free of bank conflicts.  Scales are
-// loaded once per 4 steps (16 bytes per row; four lanes per row, so their
-// dword loads coalesce into one access), staged in LDS and read as one dword
-// per row per step.  Codes are prefetched D steps ahead in registers, scales
-// one 4-step trip ahead; the steady loop is branch-free and the ragged end is
-// a guarded drain.
+// accesses, so every global load reads whole contiguous runs.  Both code
+// tiles go from global memory straight into LDS (global_load_lds_dwordx4:
+// a wave's 64 lanes fill 1 KB of LDS, lane l the 16 bytes at 16 l, with no
+// registers in between), NB buffers deep, so the loads of a step are issued
+// NB-1 steps before it runs.  Rows are stored with the 16-byte chunk index
+// XOR-swizzled by row, the permutation applied on the global side (the lane
+// that fills slot s of row r fetches the row's chunk s ^ key(r)), so that the
+// per-lane operand reads are free of bank conflicts.  Scales are loaded once
+// per 4 steps (16 bytes per row; four lanes per row, so their dword loads
+// coalesce into one access), staged in LDS and read as one dword per row per
+// step, one 4-step trip ahead; the steady loop is branch-free and the ragged
+// end is a guarded drain.
 //
-// Geometry (CDNA4, wave64): workgroup tile 256x128 (128x64 for small
-// problems), 2x2 waves, fp32 accumulators in AGPRs.  Tiles are renumbered so
-// each XCD (own L2) runs a block of GM m-tiles by consecutive n-tiles, which
+// Geometry (CDNA4, wave64): workgroup tile 256x128 with 4x2 waves of 64x64
+// (128x64 with 2x2 waves for small problems).  Tiles are renumbered so each
+// XCD (own L2) runs a block of GM m-tiles by consecutive n-tiles, which
 // bounds the W and X bytes one L2 must hold.
 #include "bsq_internal.hpp"
 #include "codec.hpp"
@@ -69,7 +72,7 @@ template <int RB> struct Swz {
   __device__ static int at(int r, int c) { return r * RB + ((c ^ key(r)) << 4); }
 };
 
-template <int FA, int FB, int BM, int BN, int WGM, int WGN, int D, int GM>
+template <int FA, int FB, int BM, int BN, int WGM, int WGN, int NB, int GM>
 __global__ void __launch_bounds__(WGM *WGN * 64)
 mxmma_kernel(const uint8_t *__restrict__ xc, const uint8_t *__restrict__ xsc, const uint8_t *__restrict__ wc,
              const uint8_t *__restrict__ wsc, void *__restrict__ out, int ot, int64_t m, int64_t n, int64_t k,
@@ -80,20 +83,21 @@ mxmma_kernel(const uint8_t *__restrict__ xc, const uint8_t *__restrict__ xsc, co
   constexpr int ABITS = MxFmt<FA>::kBits, BBITS = MxFmt<FB>::kBits;
   constexpr int XR = BK * ABITS / 8, WR = BK * BBITS / 8;  // code bytes per row per step
   constexpr int XCPR = XR / 16, WCPR = WR / 16;            // 16-byte chunks per row
-  constexpr int XCH = BM * XCPR / NTHR, WCH = BN * WCPR / NTHR;
-  constexpr int XRS = NTHR / XCPR, WRS = NTHR / WCPR;      // rows between a thread's chunks
+  constexpr int NW = WGM * WGN;
+  // the code tiles move in 1 KB blocks, one wave-wide 16-byte LDS-DMA load each
+  constexpr int XBLK = BM * XR / 1024, WBLK = BN * WR / 1024;
+  constexpr int LX = XBLK / NW, LW = WBLK / NW;  // blocks per wave per step
+  constexpr int P = NB - 1;                      // steps the DMA loads run ahead
   constexpr int SCH = TRIP * (BM + BN) / NTHR;             // scale dwords per thread per trip
   constexpr int SCX = TRIP * BM / NTHR;                    // ... of which on X rows
-  static_assert(XCH * NTHR == BM * XCPR && WCH * NTHR == BN * WCPR, "code tiles must split evenly");
+  static_assert(LX * NW == XBLK && LW * NW == WBLK && LX > 0 && LW > 0, "code tiles must split into 1 KB blocks");
+  static_assert(XCPR >= 1 && WCPR >= 1 && P >= 2, "whole chunks per row; at least two steps of lookahead");
   static_assert(SCH * NTHR == TRIP * (BM + BN) && SCX * NTHR == TRIP * BM, "scale tile must split evenly");
-  static_assert(XRS % Swz<XR>::kPeriod == 0 && WRS % Swz<WR>::kPeriod == 0, "one swizzle key per thread");
   static_assert(WTM % Swz<XR>::kPeriod == 0 && WTN % Swz<WR>::kPeriod == 0 && 32 % Swz<XR>::kPeriod == 0 &&
                     32 % Swz<WR>::kPeriod == 0,
                 "one swizzle key per lane");
-  static_assert(TRIP % D == 0, "the prefetch ring must divide a trip");
-  // three code buffers: step kt is read while step kt+1 is complete (so its
-  // first fragments can be fetched early) and step kt+2 is being written
-  constexpr int NB = 3;
+  // NB code buffers: step kt is read while step kt+1 is complete (so its
+  // first fragments can be fetched early) and steps kt+2 .. kt+P are in flight
   // scales as [step of the trip][row], the step stride padded to 16 mod 64
   // words so that the writes (4 steps x 16 rows per pass) and the per-step
   // column reads both spread over all banks
@@ -123,22 +127,25 @@ mxmma_kernel(const uint8_t *__restrict__ xc, const uint8_t *__restrict__ xsc, co
   const int64_t xrb = k * ABITS / 8, wrb = k * BBITS / 8;  // code bytes per row
   const int KT = (int)(k / BK);
 
-  // global sources of this thread's code chunks (rows past m or n read a
-  // valid row and are never stored) and their LDS destinations
-  const uint8_t *xp[XCH];
-  const uint8_t *wp[WCH];
-  const int xr0 = tid / XCPR, xc0 = tid % XCPR, wr0 = tid / WCPR, wc0 = tid % WCPR;
+  // LDS-DMA sources: block c of this wave covers LDS bytes [1024 (wu + c NW),
+  // + 1024) of a code buffer, lane l the 16 bytes at 16 l of it, i.e. slot s
+  // of row r; the row's chunk that belongs there is s ^ key(r) (rows past m
+  // or n read a valid row and are never stored)
+  const int wu = __builtin_amdgcn_readfirstlane(wid);
+  const uint8_t *xsrc[LX];
+  const uint8_t *wsrc[LW];
 #pragma unroll
-  for (int c = 0; c < XCH; ++c) {
-    const int64_t gr = m0 + xr0 + c * XRS;
-    xp[c] = xc + (gr < m ? gr : m - 1) * xrb + xc0 * 16;
+  for (int c = 0; c < LX; ++c) {
+    const int o = 1024 * (wu + c * NW) + 16 * lane, r = o / XR, s = (o % XR) >> 4;
+    const int64_t gr = m0 + r;
+    xsrc[c] = xc + (gr < m ? gr : m - 1) * xrb + ((s ^ Swz<XR>::key(r)) << 4);
   }
 #pragma unroll
-  for (int c = 0; c < WCH; ++c) {
-    const int64_t gr = n0 + wr0 + c * WRS;
-    wp[c] = wc + (gr < n ? gr : n - 1) * wrb + wc0 * 16;
+  for (int c = 0; c < LW; ++c) {
+    const int o = 1024 * (wu + c * NW) + 16 * lane, r = o / WR, s = (o % WR) >> 4;
+    const int64_t gr = n0 + r;
+    wsrc[c] = wc + (gr < n ? gr : n - 1) * wrb + ((s ^ Swz<WR>::key(r)) << 4);
   }
-  const int xd = Swz<XR>::at(xr0, xc0), wd = Swz<WR>::at(wr0, wc0);
   // scale dwords: item q = c*NTHR + tid is row q/TRIP (X rows, then W rows), step q%TRIP of a trip
   const uint8_t *sp[SCH];
   const int sst = tid % TRIP;
@@ -171,23 +178,22 @@ mxmma_kernel(const uint8_t *__restrict__ xc, const uint8_t *__restrict__ xsc, co
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  struct Slot {
-    u32x4_t x[XCH], w[WCH];
-  };
-  Slot G[D];
   uint32_t R[SCH];  // scale dwords of the next trip
 
-  auto load = [&](Slot &g, int kt) __attribute__((always_inline)) {
+  // step kt's codes straight from global memory into code buffer kt % NB
+  // (global_load_lds: no registers; counted by vmcnt until they land in LDS)
+  // (the builtin's LDS pointer type exists only in the device pass)
+  auto dma = [&](int kt) __attribute__((always_inline)) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const int b = kt % NB;
 #pragma unroll
-    for (int c = 0; c < XCH; ++c) g.x[c] = *reinterpret_cast<const u32x4_t *>(xp[c] + (int64_t)kt * XR);
+    for (int c = 0; c < LX; ++c)
+      __builtin_amdgcn_global_load_lds(xsrc[c] + (int64_t)kt * XR, smem + b * XB + 1024 * (wu + c * NW), 16, 0, 0);
 #pragma unroll
-    for (int c = 0; c < WCH; ++c) g.w[c] = *reinterpret_cast<const u32x4_t *>(wp[c] + (int64_t)kt * WR);
-  };
-  auto store = [&](const Slot &g, int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int c = 0; c < XCH; ++c) *reinterpret_cast<u32x4_t *>(&xs(buf)[xd + c * XRS * XR]) = g.x[c];
-#pragma unroll
-    for (int c = 0; c < WCH; ++c) *reinterpret_cast<u32x4_t *>(&ws(buf)[wd + c * WRS * WR]) = g.w[c];
+    for (int c = 0; c < LW; ++c)
+      __builtin_amdgcn_global_load_lds(wsrc[c] + (int64_t)kt * WR, smem + NB * XB + b * WB + 1024 * (wu + c * NW), 16,
+                                       0, 0);
+#endif
   };
   // scales of trip tr; steps past the end are clamped to the last one, so a
   // partial (or nonexistent) trip reads in bounds
@@ -248,13 +254,35 @@ mxmma_kernel(const uint8_t *__restrict__ xc, const uint8_t *__restrict__ xsc, co
   i32x8_t a0[MT], b0[NT];
   uint32_t as[MT], bs[NT];
 
+  // The step-end barrier: each wave waits until at most N of its vector
+  // memory operations are outstanding (loads complete in issue order, so the
+  // DMA loads of the step read next are in LDS), for its LDS operations, then
+  // meets the others.  Written out because __syncthreads' release fence
+  // would wait for every DMA load in flight, i.e. drain the lookahead.
+  auto bar = [&](auto Nc) __attribute__((always_inline)) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(decltype(Nc)::value) : "memory");
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  // Vector memory operations a steady step kt issues after the DMA loads of
+  // step kt+2: the DMA loads of steps kt+3 .. kt+P, and the scale loads of
+  // the steps kt+2-P .. kt that fetch a trip (step index TRIP-2 in a trip,
+  // after that step's DMA loads).
+  auto after = [](int S) constexpr {
+    int nsc = 0;
+    for (int d = 0; d <= P - 2; ++d)
+      if ((((S - d) % TRIP) + TRIP) % TRIP == TRIP - 2) ++nsc;
+    return (P - 2) * (LX + LW) + nsc * SCH;
+  };
+
   // One step kt (S = kt % TRIP).  Code buffer kt%NB holds step kt and
-  // (kt+1)%NB step kt+1 (complete since the last barrier); the register
-  // slots hold steps kt+2 .. kt+1+D, step q in slot q%D.  The step writes
-  // step kt+2 from its slot sl into buffer (kt+2)%NB, which nobody reads
-  // until after the barrier, then refills sl with the loads of step kt+2+D.
-  auto step = [&](auto guard, int kt, int S, Slot &sl) __attribute__((always_inline)) {
+  // (kt+1)%NB step kt+1 (complete since the last barrier); steps kt+2 ..
+  // kt+P-1 are on their way.  The step issues the DMA loads of step kt+P
+  // into buffer (kt+P)%NB, whose last reader (step kt-1) has passed the
+  // barrier.
+  auto step = [&](auto guard, int kt, auto Sc) __attribute__((always_inline)) {
     constexpr bool kGuard = decltype(guard)::value;
+    constexpr int S = decltype(Sc)::value;  // kt % TRIP (steady steps only)
+    const int s_ = kGuard ? kt % TRIP : S;
     const bool more = !kGuard || kt + 1 < KT;
     i32x8_t a1[MT], b1[NT];
     uint32_t asn[MT], bsn[NT];
@@ -264,16 +292,14 @@ mxmma_kernel(const uint8_t *__restrict__ xc, const uint8_t *__restrict__ xsc, co
     mma(kS0, a0, b0, as, bs);
     __builtin_amdgcn_sched_barrier(0);
     // phase 2: the next step's slice-0 fragments and scales, the slice-1
-    // MFMAs, then the LDS writes of step kt+2 (their loads have had D steps)
-    // and the global loads of step kt+2+D
+    // MFMAs, then the DMA loads of step kt+P
     if (more) {
       read((kt + 1) % NB, 0, a0, b0);
       read_sc(kt + 1, asn, bsn);
     }
     mma(kS1, a1, b1, as, bs);
-    if (!kGuard || kt + 2 < KT) store(sl, (kt + 2) % NB);
-    if (!kGuard || kt + 2 + D < KT) load(sl, kt + 2 + D);
-    if (S == TRIP - 2 && more) {
+    if (!kGuard || kt + P < KT) dma(kt + P);
+    if (s_ == TRIP - 2 && more) {
       // publish the next trip's scales one step early (the last step of this
       // trip reads them ahead), fetch the trip after
       store_sc(((kt / TRIP) + 1) & 1);
@@ -284,39 +310,34 @@ mxmma_kernel(const uint8_t *__restrict__ xc, const uint8_t *__restrict__ xsc, co
 #pragma unroll
     for (int j = 0; j < NT; ++j) bs[j] = bsn[j];
     __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
+    if constexpr (kGuard) bar(std::integral_constant<int, 0>{});
+    else bar(std::integral_constant<int, after(S)>{});
   };
   constexpr std::integral_constant<bool, false> kFast{};
   constexpr std::integral_constant<bool, true> kGuarded{};
 
-  // prologue: trip-0 scales and steps 0 and 1 into LDS, steps 2..D+1 in flight
+  // prologue: trip-0 scales in LDS, the DMA loads of steps 0 .. P-1 issued
+  // together and all waited for
   load_sc(0);
-  load(G[0], 0);
+#pragma unroll
+  for (int q = 0; q < P; ++q)
+    if (q < KT) dma(q);
   store_sc(0);
   load_sc(1);
-  store(G[0], 0);
-  if (KT > 1) {
-    load(G[0], 1);
-    store(G[0], 1);
-  }
-#pragma unroll
-  for (int q = 2; q < 2 + D; ++q)
-    if (q < KT) load(G[q % D], q);
-  __syncthreads();
+  bar(std::integral_constant<int, 0>{});
   read(0, 0, a0, b0);
   read_sc(0, as, bs);
   int kt = 0;
   // steady state: whole trips whose loads, writes and reads all stay in range
-  for (; kt + TRIP + D + 2 <= KT; kt += TRIP) {
-#pragma unroll
-    for (int S = 0; S < TRIP; ++S) step(kFast, kt + S, S, G[(S + 2) % D]);
+  for (; kt + TRIP + P <= KT; kt += TRIP) {
+    step(kFast, kt + 0, std::integral_constant<int, 0>{});
+    step(kFast, kt + 1, std::integral_constant<int, 1>{});
+    step(kFast, kt + 2, std::integral_constant<int, 2>{});
+    step(kFast, kt + 3, std::integral_constant<int, 3>{});
   }
-  // guarded drain (kt is a multiple of TRIP, hence of D, here)
-  for (; kt < KT; kt += D) {
-#pragma unroll
-    for (int S = 0; S < D; ++S)
-      if (kt + S < KT) step(kGuarded, kt + S, (kt + S) % TRIP, G[(S + 2) % D]);
-  }
+  static_assert(TRIP == 4, "the steady loop is written out for 4-step trips");
+  // guarded drain: every step waits for all its loads
+  for (; kt < KT; ++kt) step(kGuarded, kt, std::integral_constant<int, 0>{});
 
   // epilogue: the code buffers are free now; each wave stages its tile there
   static_assert(epi::stage_bytes<WTN, WGM * WGN>() <= NB * (XB + WB), "staging must fit in the code buffers");
@@ -325,11 +346,11 @@ mxmma_kernel(const uint8_t *__restrict__ xc, const uint8_t *__restrict__ xsc, co
                               n0 + wn * WTN, m, n, out, ot);
 }
 
-template <int FA, int FB, int BM, int BN, int D, int GM, int WGM = 2, int WGN = 2>
+template <int FA, int FB, int BM, int BN, int NB, int GM, int WGM = 2, int WGN = 2>
 hipError_t run_cfg(const void *xc, const void *xs, const void *wc, const void *ws, int64_t m, int64_t n, int64_t k,
                    void *out, int ot, hipStream_t s) {
   const int tiles_m = (int)((m + BM - 1) / BM), tiles_n = (int)((n + BN - 1) / BN);
-  hipLaunchKernelGGL((mxmma_kernel<FA, FB, BM, BN, WGM, WGN, D, GM>), dim3((unsigned)(tiles_m * tiles_n)),
+  hipLaunchKernelGGL((mxmma_kernel<FA, FB, BM, BN, WGM, WGN, NB, GM>), dim3((unsigned)(tiles_m * tiles_n)),
                      dim3(WGM * WGN * 64), 0,
                      s, (const uint8_t *)xc, (const uint8_t *)xs, (const uint8_t *)wc, (const uint8_t *)ws, out, ot, m,
                      n, k, tiles_m, tiles_n);
@@ -341,17 +362,20 @@ hipError_t run_ab(const void *xc, const void *xs, const void *wc, const void *ws
                   void *out, int ot, hipStream_t s) {
   if ((m + 127) / 128 * ((n + 63) / 64) > (int64_t)1 << 30) return hipErrorInvalidValue;
   const int64_t big = ((m + 255) / 256) * ((n + 127) / 128);
-  // Measured on 2048x4096x4096: one-step register prefetch everywhere; two
-  // waves per SIMD (8-wave workgroups) where the registers allow it (4-bit
-  // operands on both sides, or one 8-bit side), one wave per SIMD with both
-  // operands 8-bit (8 waves would spill).
+  // Measured on 2048x4096x4096 (us, fp4 x fp4 / e4m3 x e4m3): codes through
+  // registers with one step of prefetch 33.9 / 52.2; LDS-DMA loads 32.4 /
+  // 50.9; and 4x2 waves of 64x64 instead of 2x4 of 128x32 (fp4) and 2x2 of
+  // 128x64 (8-bit pairs; a quarter less LDS operand traffic per MFMA) 31.8 /
+  // 47.4.  NB: 4 code buffers when one step's tiles take at most 32 KB, else
+  // 3 (LDS: 160 KB per CU).
   constexpr int A8 = MxFmt<FA>::kBits == 8, B8 = MxFmt<FB>::kBits == 8;
   if (big >= 256) {
-    if constexpr (A8 && B8) return run_cfg<FA, FB, 256, 128, 1, 4, 2, 2>(xc, xs, wc, ws, m, n, k, out, ot, s);
-    else if constexpr (A8 || B8) return run_cfg<FA, FB, 256, 128, 1, 4, 4, 2>(xc, xs, wc, ws, m, n, k, out, ot, s);
-    else return run_cfg<FA, FB, 256, 128, 1, 4, 2, 4>(xc, xs, wc, ws, m, n, k, out, ot, s);
+    if constexpr (A8 && B8) return run_cfg<FA, FB, 256, 128, 3, 4, 4, 2>(xc, xs, wc, ws, m, n, k, out, ot, s);
+    else if constexpr (A8) return run_cfg<FA, FB, 256, 128, 3, 4, 4, 2>(xc, xs, wc, ws, m, n, k, out, ot, s);
+    else if constexpr (B8) return run_cfg<FA, FB, 256, 128, 4, 4, 4, 2>(xc, xs, wc, ws, m, n, k, out, ot, s);
+    else return run_cfg<FA, FB, 256, 128, 4, 4, 4, 2>(xc, xs, wc, ws, m, n, k, out, ot, s);
   }
-  return run_cfg<FA, FB, 128, 64, 1, 4, 2, 2>(xc, xs, wc, ws, m, n, k, out, ot, s);
+  return run_cfg<FA, FB, 128, 64, 3, 4, 2, 2>(xc, xs, wc, ws, m, n, k, out, ot, s);
 }
 
 template <int FA>
