@@ -39,6 +39,7 @@
 #include "bsq_internal.hpp"
 #include "codec.hpp"
 #include "epilogue.hpp"
+#include "lds_swizzle.hpp"
 
 #include <type_traits>
 
@@ -59,18 +60,6 @@ template <int F> struct MxFmt;
 template <> struct MxFmt<kMXFP8_E4M3> { static constexpr int kCode = 0, kBits = 8; };
 template <> struct MxFmt<kMXFP8_E5M2> { static constexpr int kCode = 1, kBits = 8; };
 template <> struct MxFmt<kMXFP4> { static constexpr int kCode = 4, kBits = 4; };
-
-// LDS tile with RB-byte rows: byte offset of 16-byte chunk c of row r.  The
-// chunk index is XORed with a key of the row so that 16 consecutive rows at
-// one chunk, and the chunks of consecutive rows, fall on distinct banks (a
-// 16-byte LDS access serves 16 lanes per pass over 64 banks x 4 bytes; the
-// bank-conflict counter confirms this model against a 32-bank one).
-template <int RB> struct Swz {
-  static constexpr int kCPR = RB / 16, kRPB = 256 / RB;
-  static constexpr int kPeriod = kCPR * kRPB;  // rows after which the key repeats
-  __device__ static int key(int r) { return (r / kRPB) % kCPR; }
-  __device__ static int at(int r, int c) { return r * RB + ((c ^ key(r)) << 4); }
-};
 
 template <int FA, int FB, int BM, int BN, int WGM, int WGN, int NB, int GM>
 __global__ void __launch_bounds__(WGM *WGN * 64)
