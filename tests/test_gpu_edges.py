@@ -216,14 +216,17 @@ def test_nvfp4_every_micro_scale_code_and_extreme_globals():
 def test_qgemm_mx_big_tiles(xfmt, wfmt):
     """m = 1024, n = 8192 gives 256 tiles of 256 x 128, the instantiation the
     benchmark times for each operand pair; checked on a seeded sample of rows
-    (random data, stated bound) and bit-exact on codes whose sums are exact."""
-    m, n, k = 1024, 8192, 512
+    (random data, stated bound) and bit-exact on codes whose sums are exact.
+    k = 128 and 512 leave the steady loop empty (the codes are loaded 2-3
+    steps ahead: prologue and guarded drain only); k = 2176 (17 steps) runs
+    whole 4-step trips and then a 1-step drain."""
+    m, n = 1024, 8192
     rng = np.random.default_rng(31)
     rows = np.unique(np.concatenate([[0, 255, 256, m - 1], rng.choice(m, 60, replace=False)]))
-    out, ref, den = _mx_case(xfmt, wfmt, m, n, k, seed=77, out_dtype=torch.float32, rows=rows)
-    check_bound(out, ref, den, MX_TOL, f"qgemm_mx big tiles {xfmt}x{wfmt} f32")
-    out, ref, den = _mx_case(xfmt, wfmt, m, n, k, seed=77, out_dtype=torch.bfloat16, rows=rows)
-    check_bound(out, ref, den, MX_TOL, f"qgemm_mx big tiles {xfmt}x{wfmt} bf16", True)
+    for k, od in ((512, torch.float32), (512, torch.bfloat16), (128, torch.float32), (2176, torch.bfloat16)):
+        out, ref, den = _mx_case(xfmt, wfmt, m, n, k, seed=77 + k, out_dtype=od, rows=rows)
+        check_bound(out, ref, den, MX_TOL, f"qgemm_mx big tiles {xfmt}x{wfmt} k={k} {od}", od == torch.bfloat16)
+    k = 512
     xc, xs = _exact_mx_codes(xfmt, m, k, rng)
     wc, ws = _exact_mx_codes(wfmt, n, k, rng)
     fx, fw = bsq._fmt(xfmt), bsq._fmt(wfmt)
