@@ -825,14 +825,20 @@ hipError_t run_f(const QWeight &w, int64_t m, const void *x, void *out, int ot, 
 
 // Expert-grouped rows (the routing table from grouped.hip): 128-row tiles, so
 // tiles never straddle two experts' rows; 128x256 tiles with the step-ahead
-// schedule when the widest grid gives >= 128 tiles, else 128x64.
+// schedule when the widest grid gives >= 128 tiles, else 128x64.  A grid of
+// more than 256 wide tiles (one per CU) would leave a partly filled second
+// round; there the formats whose 4-wave 128x128 kernel fits two workgroups
+// per CU take that instead (1024 tokens top-2 of 8 mxfp4 experts of 4096 x
+// 4096, 304 tiles of 128x256: 119 -> 112 us).
 template <int F>
 hipError_t run_grouped(const QWeight &w, int64_t m, const void *x, void *out, int ot, const int32_t *gtab,
                        int64_t gperm, int tiles_m, hipStream_t s) {
   const Grp g{gtab, gperm, tiles_m};
   if ((int64_t)tiles_m * ((w.n + 63) / 64) > (int64_t)1 << 30) return hipErrorInvalidValue;
-  if (w.n >= 256 && (int64_t)tiles_m * ((w.n + 255) / 256) >= 128)
-    return run_cfg<F, 128, 256, 1, 8, 1, 4, false, 5>(w, m, x, out, ot, s, g);
+  const int64_t wide = (int64_t)tiles_m * ((w.n + 255) / 256);
+  if (!kFold<F> && w.n >= 256 && wide > 256)
+    return run_cfg<F, 128, 128, 1, 4, 1, 4, false, 5>(w, m, x, out, ot, s, g);
+  if (w.n >= 256 && wide >= 128) return run_cfg<F, 128, 256, 1, 8, 1, 4, false, 5>(w, m, x, out, ot, s, g);
   return run_cfg<F, 128, 64, 2, 2, 2, 4, false, 4>(w, m, x, out, ot, s, g);
 }
 

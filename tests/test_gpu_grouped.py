@@ -106,6 +106,21 @@ def test_grouped_parity_wide_tiles(fmt, k):
     _check(fmt, p, X, ids, n, out, rows, f"wide k={k}")
 
 
+@pytest.mark.parametrize("fmt", ALL)
+def test_grouped_parity_more_than_one_round(fmt):
+    """8 experts of 3900 x 256 with 2100 rows: more than 256 wide tiles, where
+    the float formats switch to 128x128 tiles (two workgroups per CU) and
+    int4 / int8 keep the 128x256 ones; ragged n and ragged expert groups."""
+    E, n, k = 8, 3900, 256
+    p, stack = _stack(fmt, E, n, k, seed=91)
+    ids = _ids_with_counts([400, 129, 0, 383, 1, 500, 300, 387], seed=92)
+    X = workloads.random_activations(len(ids), k, seed=93, act="bf16")
+    out, st = _run(stack, E, ids, X)
+    assert st == 0
+    rows = np.sort(np.random.default_rng(94).choice(len(ids), 200, replace=False))
+    _check(fmt, p, X, ids, n, out, rows, "more than one round")
+
+
 def test_grouped_max_experts_and_single_expert():
     """1024 experts (the most the routing takes) with 1500 random rows, most
     experts holding 0-3 rows; and one expert holding every row."""
