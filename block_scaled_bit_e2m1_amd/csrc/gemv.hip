@@ -500,16 +500,20 @@ __global__ void __launch_bounds__(WPG * 64) gemv1_kernel(const GemvParams p) {
   }
 }
 
-// Measured on MI355X (graph replay, cold weights): 4-bit codes take KW = 2,
-// two sequential groups of 2 rows, 8-wave workgroups (nvfp4 4096 x 4096:
-// 3.62 us per launch; one group of 2 rows: 3.82; the one-wave-per-row-pair
-// kernel: 4.76); 8-bit codes take KW = 4, one group of 2 rows, 4 waves
-// (mxfp8 14336 x 4096: 10.7 us against a 10.1 us pure read of the codes).
+// Measured on MI355X (graph replay, cold weights, nvfp4 4096 x 4096, us per
+// launch on one box): 4-bit codes take KW = 2 and four sequential groups of 2
+// rows per wave pair in 4-wave workgroups, 16 rows each (3.75; the same 16
+// rows as two groups in 8-wave workgroups 3.88, one group of 2 rows 4.12,
+// 3 / 6 / 8 groups 4.26 / 4.25 / 4.73, groups of 4 rows 4.08-4.75, 2- or
+// 16-wave workgroups 4.26-4.7; the one-wave-per-row-pair kernel 4.76); the
+// fused RMSNorm and the routed gather gain with it (4.99 -> 4.48, 23.6 ->
+// 22.7).  8-bit codes take KW = 4, one group of 2 rows, 4 waves (mxfp8 14336
+// x 4096: 10.4 us against a 10.1 us pure read of the codes).
 template <int F>
 hipError_t run(const QWeight &w, int64_t m, const void *x, void *out, int ot, const int32_t *eids, int64_t nexp,
                int *status, hipStream_t s, const void *gam = nullptr, float eps = 0.0f) {
   constexpr bool k4 = Traits<F>::kBits == 4;
-  constexpr int KW = k4 ? 2 : 4, R = 2, S = k4 ? 2 : 1, WPG = k4 ? 8 : 4;
+  constexpr int KW = k4 ? 2 : 4, R = 2, S = k4 ? 4 : 1, WPG = 4;
   constexpr int rows_per_wg = (WPG / KW) * R * S;
   const int64_t wgs = (w.n + rows_per_wg - 1) / rows_per_wg;
   if (wgs > 0x7FFFFFFF || m > 65535) return hipErrorInvalidValue;
