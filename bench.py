@@ -578,7 +578,7 @@ def main():
                          "bytes; register-only bf16 MFMA loop) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (this build has no multi-GPU "
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (the library has no multi-GPU "
               f"path; the decode/prefill kernels shard along n with no exchange step).", file=sys.stderr)
         sys.exit(2)
 

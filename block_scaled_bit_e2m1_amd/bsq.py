@@ -52,7 +52,7 @@ def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+            raise ImportError(f"{LIB_PATH} is missing: build it with python -m block_scaled_bit_e2m1_amd.build")
         L = ctypes.CDLL(LIB_PATH)
         L.bsq_packed_bytes.argtypes = [_c_int, _c_int, _i64, _i64, _sz, _sz, _sz]
         L.bsq_pack_host.argtypes = [_c_int, _c_int, _vp, _i64, _i64, _vp, _vp, _vp, ctypes.POINTER(_f32)]
