@@ -19,7 +19,7 @@ for the timed kernel, and the CPU oracle timed on a bounded sample as
 `cpu_baseline`.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-extra] [--no-cpu] [--only-timed] [--mx-only] [--grouped-only]
+                    [--no-extra] [--no-cpu] [--only-timed] [--mx-only] [--grouped-only] [--moe-decode-only]
 """
 from __future__ import annotations
 
@@ -402,6 +402,40 @@ def time_gather_qmm(device, fmt="mxfp4", E=8, n=14336, k=4096, ids=(1, 6, 2, 5))
             "roofline_frac": round(wb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def time_moe_decode_shared(device, fmt="mxfp4", E=8, n=14336, k=4096, ids=(1, 6, 2, 5) * 4):
+    """Decode-sized MoE where tokens share experts (8 tokens, top-2, all on 4
+    of the 8 experts): the expert-grouped call (decode form: one pass over
+    each routed expert for all its rows) against the per-row gather (one pass
+    per routed row).  Rate = weight bytes of the distinct routed experts per
+    launch / time; three expert stacks rotated so launches read HBM."""
+    import torch
+
+    from block_scaled_bit_e2m1_amd import bsq, workloads
+
+    pw = bsq.pack(fmt, workloads.random_weights(E * n, k, seed=1005, sigma=0.02))
+    copies = max(1, min(3, ROTATE_BYTES // pw.weight_bytes + 1))
+    stacks = [bsq.to_device(pw, device) for _ in range(copies)]
+    m = len(ids)
+    x = torch.from_numpy(workloads.random_activations(m, k, seed=1006, act="bf16")).to(torch.bfloat16).to(device)
+    eids = torch.tensor(ids, dtype=torch.int32, device=device)
+    out = torch.empty((m, n), dtype=torch.bfloat16, device=device)
+    st, need = bsq.bsq_grouped_qgemm_workspace(m, E)
+    assert st == bsq.OK
+    ws = torch.empty(max(need, 4), dtype=torch.uint8, device=device)
+    it, it2 = iter(range(1 << 62)), iter(range(1 << 62))
+    reps = max(1, 600 // copies)
+    us = graph_event_ms(lambda: bsq.grouped_qmm(stacks[next(it) % copies], E, eids, x, out=out, workspace=ws), copies,
+                        reps, device) * 1e3
+    us_gather = graph_event_ms(lambda: bsq.gather_qmm(stacks[next(it2) % copies], E, eids, x, out=out), copies,
+                               reps, device) * 1e3
+    wb = len(set(ids)) * pw.weight_bytes // E
+    return {"workload": f"moe_decode_shared_{fmt}_{E}x{n}x{k}_rows{m}_experts{len(set(ids))}",
+            "note": "decode MoE, tokens sharing experts: expert-grouped call (decode form: one pass per routed expert) "
+                    "vs the per-row gather (one pass per routed row)",
+            "value": round(wb / (us * 1e-6) / 1e9, 2), "unit": "GB/s", "us_per_launch": round(us, 3),
+            "roofline_frac": round(wb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "us_per_launch_gather": round(us_gather, 3)}
+
+
 def time_grouped_qmm(device, name="mxfp4_moe_prefill_8x4096", reps=200):
     """Prefill MoE step (bsq_grouped_qgemm): the routing kernel, then the
     grouped MFMA GEMM over 128-row tiles of each expert's rows, bf16 out.  One
@@ -570,6 +604,8 @@ def main():
     ap.add_argument("--only-timed", action="store_true", help="timed workload only (for profiling)")
     ap.add_argument("--mx-only", action="store_true", help="only time the scaled-MFMA GEMMs and exit")
     ap.add_argument("--grouped-only", action="store_true", help="only time the prefill MoE grouped GEMM and exit")
+    ap.add_argument("--moe-decode-only", action="store_true",
+                    help="only time the decode MoE with shared experts (grouped call vs gather) and exit")
     ap.add_argument("--mx-pair", default="", help="with --mx-only: one pair XFMT,WFMT (e.g. mxfp4,mxfp4)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="only run torch's copy kernel on MIB MiB (counter calibration) and exit")
@@ -620,6 +656,9 @@ def main():
         pairs = [tuple(args.mx_pair.split(","))] if args.mx_pair else MX_PAIRS
         for xf, wf in pairs:
             print(json.dumps(time_qgemm_mx(device, xf, wf, reps=max(1, args.steps // 8))), flush=True)
+        return
+    if args.moe_decode_only:
+        print(json.dumps(time_moe_decode_shared(device)), flush=True)
         return
     if args.grouped_only:
         print(json.dumps(time_grouped_qmm(device, reps=max(4, args.steps))), flush=True)
@@ -690,9 +729,11 @@ def main():
 
     if not args.no_extra and not args.only_timed:
         extra.append(time_quantize(device))
-        for e in (time_rmsnorm_qgemv(device), time_gather_qmm(device)):
+        for e in (time_rmsnorm_qgemv(device), time_gather_qmm(device), time_moe_decode_shared(device)):
             extra.append(e)
-            log(f"  {e['workload']}: {e['value']:.1f} GB/s ({e['us_per_launch']:.2f} us/launch)")
+            log(f"  {e['workload']}: {e['value']:.1f} GB/s ({e['us_per_launch']:.2f} us/launch)"
+                + (f", per-row gather {e['us_per_launch_gather']:.2f} us" if 'us_per_launch_gather' in e else ""))
+        torch.cuda.empty_cache()
         e = time_grouped_qmm(device)
         extra.append(e)
         log(f"  {e['workload']}: {e['value']:.1f} TFLOP/s ({e['us_per_launch']:.2f} us/launch)")

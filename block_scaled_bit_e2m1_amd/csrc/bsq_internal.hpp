@@ -69,6 +69,17 @@ hipError_t launch_gemv(const QWeight &w, int64_t m, const void *x, void *out, in
 bool gemv_norm_applies(const QWeight &w, int64_t m, int xt);
 hipError_t launch_gemv_norm(const QWeight &w, const void *x, const void *gam, float eps, void *out, int ot,
                             hipStream_t s);
+// The decode form of the expert-grouped matmul on the decode GEMV kernel
+// (gemv.hip): routed in the kernel itself, tiles of up to kGemvGroupRows rows
+// of one expert, one pass over the expert's weight per tile; bad ids zero
+// their rows and set *status (may be null) to 1.  Applies to m up to
+// kGemvGroupMaxRows and the one-round shape (k = 4096 for every format) with
+// 31-bit offsets of the stacked weight and of the m rows.
+constexpr int kGemvGroupRows = 4;
+constexpr int64_t kGemvGroupMaxRows = 32;
+bool gemv_grouped_applies(const QWeight &w, int64_t m, int64_t nexp);
+hipError_t launch_gemv_grouped(const QWeight &w, int64_t m, int64_t nexp, const int32_t *eids, const void *x,
+                               void *out, int ot, int *status, hipStream_t s);
 // MFMA kernel: bf16 X, any m >= 1.
 hipError_t launch_mfma(const QWeight &w, int64_t m, const void *x, void *out, int ot, hipStream_t s);
 // Zero-fill an output of `bytes` bytes (k == 0 case).

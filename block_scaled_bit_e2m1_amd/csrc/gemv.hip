@@ -39,6 +39,7 @@
 #include "codec.hpp"
 #include "dot.hpp"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace bsq {
@@ -500,6 +501,145 @@ __global__ void __launch_bounds__(WPG * 64) gemv1_kernel(const GemvParams p) {
   }
 }
 
+// The decode form of the expert-grouped matmul: one pass over an expert's
+// weight rows serves up to T of the rows routed to it, where the per-row
+// gather streams the expert once per routed row.
+//
+// The routing is done in the kernel (m <= 64: every id fits one wave): each
+// wave loads the ids, counts for every row the earlier rows of the same
+// expert, and takes as tile leaders the valid rows whose count is a multiple
+// of T; a tile is its leader and the next T - 1 rows (in row order) of the
+// leader's expert.  Grid y enumerates the leaders (WGs past their number exit
+// at once); all of it is uniform, in scalar registers.  Rows whose id is
+// outside [0, E) are zeroed by the workgroups of y = 0 and set *status to 1.
+//
+// Each tile runs the body for its own row count (1, 2 or 4 rows; 3 takes the
+// 4-row body with its last row repeated and not stored), so a lone row costs
+// what the per-row kernel does.  Same geometry and one-round shape as
+// gemv1_kernel; every lane holds its chunk's activations of the tile's rows,
+// and the weight chunk is decoded once for all of them (the conversions are
+// pure operations on the same words, so the compiler emits them once).
+template <int F, int KW, int R, int S, int WPG, int T>
+__device__ __forceinline__ void gemvg_body(const GemvParams &p, const int (&tok)[4], int nr, int e,
+                                           float (*red)[R * S * 4]) {
+  constexpr int E = kE<F>, XQ = E / 8, RG = WPG / KW, RS = R * S;
+  constexpr int SB = (F == kNVFP8 || F == kINT8_SYM) ? 4 : (F == kINT4_AFFINE ? 2 : 1);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int rg = w / KW, ks = w - rg * KW;
+  const int n = (int)p.n;
+  const int rowb = (int)p.rowb, srowb = (int)p.srowb;
+  const int j0 = (blockIdx.x * RG + rg) * RS;
+  const int ch = ks * 64 + lane;
+  const int jbase = e * n;
+  v4u cw[S][R];
+  uint32_t sw[S][R], bw[S][R];
+  uint4 xq[T][XQ];
+  auto load_group = [&](int s) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int jr = jbase + min(j0 + s * R + r, n - 1);  // rows past n: read row n-1, never stored
+      bw[s][r] = 0u;
+      load_sc<F>(p.scales + (size_t)jr * srowb, p.biases + (size_t)jr * (srowb / SB), (uint32_t)ch, sw[s][r], bw[s][r]);
+      cw[s][r] = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p.codes + (size_t)jr * rowb) + ch);
+    }
+  };
+  load_group(0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const uint16_t *xr = p.x + (size_t)tok[t] * (size_t)p.k;
+#pragma unroll
+    for (int q = 0; q < XQ; ++q) xq[t][q] = reinterpret_cast<const uint4 *>(xr + ch * E)[q];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int s = 1; s < S; ++s) load_group(s);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    float acc[T][R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      asm volatile("" : "+v"(cw[s][r]), "+v"(sw[s][r]));
+#pragma unroll
+      for (int t = 0; t < T; ++t) acc[t][r] = chunk_dot<F>(cw[s][r], sw[s][r], bw[s][r], xq[t], 0.0f);
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const float v = joint_sum<R>(acc[t]);
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (lane == out_lane<R>(r)) red[w][t * RS + s * R + r] = v;
+    }
+  }
+  __syncthreads();
+  if (ks == 0 && lane < RS * T) {
+    const int t = lane / RS, jj = lane - t * RS;
+    if (t < nr && j0 + jj < n) {
+      float v = 0.0f;
+#pragma unroll
+      for (int q = 0; q < KW; ++q) v += red[rg * KW + q][lane];
+      if constexpr (F == kNVFP4) v *= p.global;
+      const size_t o = (size_t)tok[t] * (size_t)n + j0 + jj;
+      if (p.ot == 0) reinterpret_cast<float *>(p.out)[o] = v;
+      else reinterpret_cast<uint16_t *>(p.out)[o] = f32_to_bf16_bits(v);
+    }
+  }
+}
+
+template <int F, int KW, int R, int S, int WPG>
+__global__ void __launch_bounds__(WPG * 64) gemvg_kernel(const GemvParams p, int m) {
+  constexpr int T = kGemvGroupRows, RG = WPG / KW, RS = R * S;
+  static_assert(KW > 1 && T == 4 && RS * T <= 64, "the k-split combine stores one sum per lane");
+  __shared__ float red[WPG][RS * T];
+  constexpr int MM = (int)kGemvGroupMaxRows;
+  const int lane = threadIdx.x & 63;
+  // The ids through the scalar unit: uniform loads that, after the first
+  // workgroup on a CU, hit its scalar cache, so a workgroup with no tile
+  // leaves after a short wait.  Lane j takes row j's expert and counts the
+  // earlier rows of the same expert.
+  int ids[MM];
+#pragma unroll
+  for (int j = 0; j < MM; ++j) ids[j] = j < m ? p.eids[j] : -1;
+  int el = -1, rank = 0;
+#pragma unroll
+  for (int j = 0; j < MM; ++j) el = lane == j ? ids[j] : el;
+#pragma unroll
+  for (int j = 0; j < MM; ++j) rank += (j < lane && ids[j] == el) ? 1 : 0;
+  const bool valid = lane < m && el >= 0 && (int64_t)el < p.nexp;
+  if (blockIdx.y == 0) {
+    const uint64_t bad = __ballot(lane < m && !valid);
+    if (bad) {
+      if (p.status && blockIdx.x == 0 && threadIdx.x == 0) *p.status = 1;
+      const int c0 = blockIdx.x * RG * RS, n = (int)p.n;
+      for (uint64_t b = bad; b; b &= b - 1) {
+        const int i = __builtin_ctzll(b);
+        for (int c = threadIdx.x; c < RG * RS && c0 + c < n; c += WPG * 64) {
+          const size_t o = (size_t)i * (size_t)n + c0 + c;
+          if (p.ot == 0) reinterpret_cast<float *>(p.out)[o] = 0.0f;
+          else reinterpret_cast<uint16_t *>(p.out)[o] = 0;
+        }
+      }
+    }
+  }
+  uint64_t lead = __ballot(valid && rank % T == 0);
+  if ((int)blockIdx.y >= __popcll(lead)) return;  // uniform: no tile for this y
+  for (unsigned q = 0; q < blockIdx.y; ++q) lead &= lead - 1;
+  const int p0 = __builtin_ctzll(lead);
+  const int e = __builtin_amdgcn_readlane(el, p0);
+  uint64_t same = (__ballot(valid && el == e) >> p0) & ~(uint64_t)1;  // the expert's rows after the leader
+  int tok[4] = {p0, p0, p0, p0}, nr = 1;
+#pragma unroll
+  for (int t = 1; t < 4; ++t) {
+    tok[t] = same ? p0 + __builtin_ctzll(same) : tok[t - 1];
+    nr += same ? 1 : 0;
+    same &= same - 1;
+  }
+  if (nr == 1) gemvg_body<F, KW, R, S, WPG, 1>(p, tok, nr, e, red);
+  else if (nr == 2) gemvg_body<F, KW, R, S, WPG, 2>(p, tok, nr, e, red);
+  else gemvg_body<F, KW, R, S, WPG, 4>(p, tok, nr, e, red);
+}
+
 // Measured on MI355X (graph replay, cold weights, nvfp4 4096 x 4096, us per
 // launch on one box): 4-bit codes take KW = 2 and four sequential groups of 2
 // rows per wave pair in 4-wave workgroups, 16 rows each (3.75; the same 16
@@ -510,6 +650,26 @@ __global__ void __launch_bounds__(WPG * 64) gemv1_kernel(const GemvParams p) {
 // 22.7).  8-bit codes take KW = 4, one group of 2 rows, 4 waves (mxfp8 14336
 // x 4096: 10.4 us against a 10.1 us pure read of the codes).
 template <int F>
+GemvParams params(const QWeight &w, const void *x, void *out, int ot) {
+  constexpr bool k4 = Traits<F>::kBits == 4;
+  constexpr int SB = (F == kNVFP8 || F == kINT8_SYM) ? 4 : (F == kINT4_AFFINE ? 2 : 1);
+  GemvParams p{};
+  p.codes = (const uint8_t *)w.codes;
+  p.scales = (const uint8_t *)w.scales;
+  p.biases = (const uint16_t *)w.biases;
+  p.x = (const uint16_t *)x;
+  p.out = out;
+  p.n = w.n;
+  p.k = w.k;
+  p.rowb = (uint64_t)(k4 ? w.k / 2 : w.k);
+  p.srowb = (uint64_t)(w.k / Traits<F>::kBlock) * SB;
+  p.global = w.global;
+  p.ot = ot;
+  p.C = (int)(w.k / (k4 ? 32 : 16));
+  return p;
+}
+
+template <int F>
 hipError_t run(const QWeight &w, int64_t m, const void *x, void *out, int ot, const int32_t *eids, int64_t nexp,
                int *status, hipStream_t s, const void *gam = nullptr, float eps = 0.0f) {
   constexpr bool k4 = Traits<F>::kBits == 4;
@@ -517,24 +677,10 @@ hipError_t run(const QWeight &w, int64_t m, const void *x, void *out, int ot, co
   constexpr int rows_per_wg = (WPG / KW) * R * S;
   const int64_t wgs = (w.n + rows_per_wg - 1) / rows_per_wg;
   if (wgs > 0x7FFFFFFF || m > 65535) return hipErrorInvalidValue;
-  // every byte offset of the (stacked) weight in 31 bits: 32-bit index math
-  GemvParams p;
-  p.codes = (const uint8_t *)w.codes;
-  p.scales = (const uint8_t *)w.scales;
-  p.biases = (const uint16_t *)w.biases;
-  p.x = (const uint16_t *)x;
-  p.out = out;
+  GemvParams p = params<F>(w, x, out, ot);
   p.eids = eids;
   p.status = status;
-  p.n = w.n;
-  p.k = w.k;
   p.nexp = nexp;
-  p.rowb = (uint64_t)(k4 ? w.k / 2 : w.k);
-  constexpr int SB = (F == kNVFP8 || F == kINT8_SYM) ? 4 : (F == kINT4_AFFINE ? 2 : 1);
-  p.srowb = (uint64_t)(w.k / Traits<F>::kBlock) * SB;
-  p.global = w.global;
-  p.ot = ot;
-  p.C = (int)(w.k / (k4 ? 32 : 16));
   p.g = (const uint16_t *)gam;
   p.eps = eps;
   const int64_t total_rows = w.n * (eids ? nexp : 1);
@@ -553,7 +699,51 @@ hipError_t run(const QWeight &w, int64_t m, const void *x, void *out, int ot, co
   return hipGetLastError();
 }
 
+// The grouped decode form: the one-round geometry of run(), one grid row per
+// possible tile.
+template <int F>
+hipError_t run_grouped(const QWeight &w, int64_t m, int64_t nexp, const int32_t *eids, const void *x, void *out,
+                       int ot, int *status, hipStream_t s) {
+  constexpr bool k4 = Traits<F>::kBits == 4;
+  constexpr int KW = k4 ? 2 : 4, R = 2, S = k4 ? 4 : 1, WPG = 4;
+  constexpr int rows_per_wg = (WPG / KW) * R * S;
+  const int64_t wgs = (w.n + rows_per_wg - 1) / rows_per_wg;
+  if (wgs > 0x7FFFFFFF || m < 1 || m > kGemvGroupMaxRows) return hipErrorInvalidValue;
+  GemvParams p = params<F>(w, x, out, ot);
+  p.eids = eids;
+  p.nexp = nexp;
+  p.status = status;
+  // tiles: sum over the D routed experts of ceil(rows / T) <= (m + (T - 1) D) / T, D <= min(E, m); and <= m
+  constexpr int T = kGemvGroupRows;
+  const int64_t tiles = std::min<int64_t>(m, (m + (T - 1) * std::min(nexp, m)) / T);
+  hipLaunchKernelGGL((gemvg_kernel<F, KW, R, S, WPG>), dim3((unsigned)wgs, (unsigned)tiles), dim3(WPG * 64), 0, s,
+                     p, (int)m);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+bool gemv_grouped_applies(const QWeight &w, int64_t m, int64_t nexp) {
+  // decode-sized m, the one-round shape (64 chunks per wave of the k split), 31-bit offsets
+  const bool k4 = is_4bit(w.fmt);
+  const int64_t E = k4 ? 32 : 16, KW = k4 ? 2 : 4, rowb = k4 ? w.k / 2 : w.k;
+  return m >= 1 && m <= kGemvGroupMaxRows && w.k == 64 * KW * E && w.n * nexp * rowb < ((int64_t)1 << 31) &&
+         m * w.k < ((int64_t)1 << 30);
+}
+
+hipError_t launch_gemv_grouped(const QWeight &w, int64_t m, int64_t nexp, const int32_t *eids, const void *x,
+                               void *out, int ot, int *status, hipStream_t s) {
+  switch (w.fmt) {
+    case kMXFP4: return run_grouped<kMXFP4>(w, m, nexp, eids, x, out, ot, status, s);
+    case kNVFP4: return run_grouped<kNVFP4>(w, m, nexp, eids, x, out, ot, status, s);
+    case kMXFP8_E4M3: return run_grouped<kMXFP8_E4M3>(w, m, nexp, eids, x, out, ot, status, s);
+    case kMXFP8_E5M2: return run_grouped<kMXFP8_E5M2>(w, m, nexp, eids, x, out, ot, status, s);
+    case kNVFP8: return run_grouped<kNVFP8>(w, m, nexp, eids, x, out, ot, status, s);
+    case kINT4_AFFINE: return run_grouped<kINT4_AFFINE>(w, m, nexp, eids, x, out, ot, status, s);
+    case kINT8_SYM: return run_grouped<kINT8_SYM>(w, m, nexp, eids, x, out, ot, status, s);
+  }
+  return hipErrorInvalidValue;
+}
 
 bool gemv_applies(const QWeight &w, int64_t m, int xt, bool routed) {
   // bf16 activations, whole 16-byte code chunks, one weight pass per row

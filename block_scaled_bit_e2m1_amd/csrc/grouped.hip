@@ -15,6 +15,9 @@
 //     is outside [0, E) are written as zeros and flag *status.
 //  2. mfma_kernel in its grouped form (mfma.hip): X rows gathered and output
 //     rows scattered through the table; tiles past the count exit at once.
+// Decode-sized m on the decode GEMV shapes skips both: the GEMV kernel's
+// grouped form (gemv.hip) routes the few rows itself and streams each
+// expert's weight once per tile of up to 4 of its rows.
 // The order of rows inside an expert's group comes from LDS atomics, but every
 // output row is computed the same way wherever it sits, so the result is
 // bit-for-bit the same from run to run.
@@ -150,6 +153,7 @@ int64_t grouped_workspace_bytes(int64_t m, int64_t nexp) { return 4 * table_word
 
 hipError_t launch_grouped(const QWeight &w, int64_t m, int64_t nexp, const int32_t *eids, const void *x, void *out,
                           int ot, void *workspace, int *status, hipStream_t s) {
+  if (gemv_grouped_applies(w, m, nexp)) return launch_gemv_grouped(w, m, nexp, eids, x, out, ot, status, s);
   int32_t *table = reinterpret_cast<int32_t *>(workspace);
   const int64_t poff = perm_offset(m, nexp);
   hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), 0, s, eids, m, (int)nexp, table, poff, out, ot,

@@ -5,7 +5,9 @@ so the oracle is oracle.gather_matmul on the same seeded inputs, to the
 bf16 bound |gpu - ref| <= 2e-3 * sum|x*w| per output.  The cases span experts
 with no rows, one row, a ragged multiple of the 128-row tile, ragged n and k
 (both tile configurations), the largest expert count, ids outside the stack,
-graph replay, and the prefill MoE workload at full size on sampled rows.  The
+graph replay, the decode form (m <= 32, k = 4096: routed inside the GEMV
+kernel) with shared, lone and bad ids, and the prefill MoE workload at full
+size on sampled rows.  The
 output and the workspace sit between guard bands that must come back
 untouched.
 """
@@ -119,6 +121,63 @@ def test_grouped_parity_more_than_one_round(fmt):
     assert st == 0
     rows = np.sort(np.random.default_rng(94).choice(len(ids), 200, replace=False))
     _check(fmt, p, X, ids, n, out, rows, "more than one round")
+
+
+@pytest.mark.parametrize("fmt", ALL)
+def test_grouped_decode_form(fmt):
+    """m <= 32 routed rows on the decode GEMV shape (k = 4096) take the
+    decode form (routed in the kernel, tiles of up to 4 rows of one expert,
+    one weight pass per tile): 4 experts of 1000 x 4096 (ragged against every
+    row group) with rows shared between tokens; m = 1, 5 (tiles of 2 and 3
+    rows), 19 (an expert with 9 rows spans three tiles) and 32; bf16 and f32
+    output."""
+    E, n, k = 4, 1000, 4096
+    p, stack = _stack(fmt, E, n, k, seed=61)
+    W = oracle.dequant_packed(p)
+    for counts in ([1, 0, 0, 0], [2, 0, 3, 0], [9, 4, 0, 6], [8, 8, 8, 8]):
+        ids = _ids_with_counts(counts, seed=62 + sum(counts))
+        X = workloads.random_activations(len(ids), k, seed=63 + len(ids), act="bf16")
+        ref, den = oracle.gather_matmul(X, W, ids, n)
+        for dt in (torch.bfloat16, torch.float32):
+            out, st = _run(stack, E, ids, X, dt)
+            assert st == 0
+            check_bound(out, ref, den, 2e-3, f"grouped decode {fmt} m={len(ids)} {dt}", dt == torch.bfloat16)
+
+
+def test_grouped_small_m_off_the_decode_shape():
+    """m <= 32 with k other than 4096 keeps the 128-row MFMA tiles: 3 experts
+    of 300 x 512, 7 rows."""
+    E, n, k = 3, 300, 512
+    p, stack = _stack("nvfp4", E, n, k, seed=66)
+    ids = _ids_with_counts([3, 0, 4], seed=67)
+    X = workloads.random_activations(len(ids), k, seed=68, act="bf16")
+    out, st = _run(stack, E, ids, X)
+    assert st == 0
+    _check("nvfp4", p, X, ids, n, out, what="small m, k = 512")
+
+
+def test_grouped_decode_form_bad_ids_and_equal_to_gather():
+    """Decode-sized m with ids outside [0, E): those rows are zero and the
+    status is set; every other row meets the bound against the oracle, as
+    the per-row gather of the same rows does.  Calls with no valid id at all
+    give all-zero outputs."""
+    E, n, k = 6, 600, 4096
+    p, stack = _stack("mxfp4", E, n, k, seed=64)
+    ids = np.array([3, -1, 3, 5, 0, 6, 3, 5, 0, 3], np.int32)
+    X = workloads.random_activations(len(ids), k, seed=65, act="bf16")
+    out, st = _run(stack, E, ids, X)
+    assert st == 1
+    bad = (ids < 0) | (ids >= E)
+    assert (out[bad] == 0).all()
+    good = ~bad
+    x = torch.from_numpy(np.ascontiguousarray(X[good])).to(torch.bfloat16).to(DEV)
+    g = bsq.gather_qmm(stack, E, torch.from_numpy(ids[good]).to(DEV), x).float().cpu().numpy()
+    ref, den = oracle.gather_matmul(X[good], oracle.dequant_packed(p), ids[good], n)
+    check_bound(out[good], ref, den, 2e-3, "grouped decode vs oracle", True)
+    check_bound(g, ref, den, 2e-3, "gather vs oracle", True)
+    for ids in (np.array([7], np.int32), np.array([-3, 6, 99], np.int32)):  # no valid row at all
+        out, st = _run(stack, E, ids, X[:len(ids)], torch.float32)
+        assert st == 1 and (out == 0).all()
 
 
 def test_grouped_max_experts_and_single_expert():
