@@ -73,8 +73,8 @@ hipError_t launch_gemv_norm(const QWeight &w, const void *x, const void *gam, fl
 // (gemv.hip): routed in the kernel itself, tiles of up to kGemvGroupRows rows
 // of one expert, one pass over the expert's weight per tile; bad ids zero
 // their rows and set *status (may be null) to 1.  Applies to m up to
-// kGemvGroupMaxRows and the one-round shape (k = 4096 for every format) with
-// 31-bit offsets of the stacked weight and of the m rows.
+// kGemvGroupMaxRows, whole 16-byte code chunks, and 31-bit offsets of the
+// stacked weight and of the m rows.
 constexpr int kGemvGroupRows = 4;
 constexpr int64_t kGemvGroupMaxRows = 32;
 bool gemv_grouped_applies(const QWeight &w, int64_t m, int64_t nexp);

@@ -515,11 +515,13 @@ __global__ void __launch_bounds__(WPG * 64) gemv1_kernel(const GemvParams p) {
 //
 // Each tile runs the body for its own row count (1, 2 or 4 rows; 3 takes the
 // 4-row body with its last row repeated and not stored), so a lone row costs
-// what the per-row kernel does.  Same geometry and one-round shape as
-// gemv1_kernel; every lane holds its chunk's activations of the tile's rows,
-// and the weight chunk is decoded once for all of them (the conversions are
-// pure operations on the same words, so the compiler emits them once).
-template <int F, int KW, int R, int S, int WPG, int T>
+// what the per-row kernel does.  Same geometry as the per-row kernels: one
+// round when k is 64 chunks per wave of the k split (k = 4096), else
+// guarded rounds as in gemv_kernel.  Every lane holds its chunk's activations
+// of the tile's rows, and the weight chunk is decoded once for all of them
+// (the conversions are pure operations on the same words, so the compiler
+// emits them once).
+template <int F, int KW, int R, int S, int WPG, int T, bool ONE>
 __device__ __forceinline__ void gemvg_body(const GemvParams &p, const int (&tok)[4], int nr, int e,
                                            float (*red)[R * S * 4]) {
   constexpr int E = kE<F>, XQ = E / 8, RG = WPG / KW, RS = R * S;
@@ -529,47 +531,82 @@ __device__ __forceinline__ void gemvg_body(const GemvParams &p, const int (&tok)
   const int n = (int)p.n;
   const int rowb = (int)p.rowb, srowb = (int)p.srowb;
   const int j0 = (blockIdx.x * RG + rg) * RS;
-  const int ch = ks * 64 + lane;
   const int jbase = e * n;
-  v4u cw[S][R];
-  uint32_t sw[S][R], bw[S][R];
-  uint4 xq[T][XQ];
-  auto load_group = [&](int s) {
+  float acc[S][T][R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int jr = jbase + min(j0 + s * R + r, n - 1);  // rows past n: read row n-1, never stored
-      bw[s][r] = 0u;
-      load_sc<F>(p.scales + (size_t)jr * srowb, p.biases + (size_t)jr * (srowb / SB), (uint32_t)ch, sw[s][r], bw[s][r]);
-      cw[s][r] = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p.codes + (size_t)jr * rowb) + ch);
-    }
-  };
-  load_group(0);
-  __builtin_amdgcn_sched_barrier(0);
+  for (int s = 0; s < S; ++s)
 #pragma unroll
-  for (int t = 0; t < T; ++t) {
-    const uint16_t *xr = p.x + (size_t)tok[t] * (size_t)p.k;
+    for (int t = 0; t < T; ++t)
 #pragma unroll
-    for (int q = 0; q < XQ; ++q) xq[t][q] = reinterpret_cast<const uint4 *>(xr + ch * E)[q];
-  }
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int s = 1; s < S; ++s) load_group(s);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int s = 0; s < S; ++s) {
-    float acc[T][R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      asm volatile("" : "+v"(cw[s][r]), "+v"(sw[s][r]));
-#pragma unroll
-      for (int t = 0; t < T; ++t) acc[t][r] = chunk_dot<F>(cw[s][r], sw[s][r], bw[s][r], xq[t], 0.0f);
-    }
+      for (int r = 0; r < R; ++r) acc[s][t][r] = 0.0f;
+  // Group s is complete: reduce its R rows jointly for every tile row and
+  // leave the sums in LDS for the k-split combine.
+  auto finish = [&](int s) {
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      const float v = joint_sum<R>(acc[t]);
+      const float v = joint_sum<R>(acc[s][t]);
 #pragma unroll
       for (int r = 0; r < R; ++r)
         if (lane == out_lane<R>(r)) red[w][t * RS + s * R + r] = v;
+    }
+  };
+  // One round: lane l takes chunk ch of every row of the wave's groups (a
+  // chunk past the row, in a wave's last round, loads chunk 0 and adds
+  // nothing).  In the wave's last round each group is reduced as soon as its
+  // dots are done, overlapping the arrival of the later groups' data.
+  auto round = [&](int ch, bool in, bool last) {
+    const int cc = in ? ch : 0;
+    v4u cw[S][R];
+    uint32_t sw[S][R], bw[S][R];
+    uint4 xq[T][XQ];
+    auto load_group = [&](int s) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int jr = jbase + min(j0 + s * R + r, n - 1);  // rows past n: read row n-1, never stored
+        bw[s][r] = 0u;
+        load_sc<F>(p.scales + (size_t)jr * srowb, p.biases + (size_t)jr * (srowb / SB), (uint32_t)cc, sw[s][r],
+                   bw[s][r]);
+        cw[s][r] = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p.codes + (size_t)jr * rowb) + cc);
+      }
+    };
+    load_group(0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const uint16_t *xr = p.x + (size_t)tok[t] * (size_t)p.k;
+#pragma unroll
+      for (int q = 0; q < XQ; ++q) xq[t][q] = reinterpret_cast<const uint4 *>(xr + cc * E)[q];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 1; s < S; ++s) load_group(s);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      if (ONE || in) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          asm volatile("" : "+v"(cw[s][r]), "+v"(sw[s][r]));
+#pragma unroll
+          for (int t = 0; t < T; ++t) acc[s][t][r] = chunk_dot<F>(cw[s][r], sw[s][r], bw[s][r], xq[t], acc[s][t][r]);
+        }
+      }
+      if (ONE || last) finish(s);
+    }
+  };
+  if constexpr (ONE) {
+    round(ks * 64 + lane, true, true);
+  } else {
+    // this wave's rounds: chunks ks * 64 + lane + i * 64 * KW below C
+    const int C = p.C, first = ks * 64;
+    const int nround = C > first ? (C - first + 64 * KW - 1) / (64 * KW) : 0;
+    for (int i = 0; i + 1 < nround; ++i) round(first + i * 64 * KW + lane, true, false);
+    if (nround > 0) {
+      const int ch = first + (nround - 1) * 64 * KW + lane;
+      round(ch, ch < C, true);
+    } else {
+#pragma unroll
+      for (int q = 0; q < S; ++q) finish(q);  // k shorter than the split: this wave adds zeros
     }
   }
   __syncthreads();
@@ -587,7 +624,7 @@ __device__ __forceinline__ void gemvg_body(const GemvParams &p, const int (&tok)
   }
 }
 
-template <int F, int KW, int R, int S, int WPG>
+template <int F, int KW, int R, int S, int WPG, bool ONE>
 __global__ void __launch_bounds__(WPG * 64) gemvg_kernel(const GemvParams p, int m) {
   constexpr int T = kGemvGroupRows, RG = WPG / KW, RS = R * S;
   static_assert(KW > 1 && T == 4 && RS * T <= 64, "the k-split combine stores one sum per lane");
@@ -635,9 +672,9 @@ __global__ void __launch_bounds__(WPG * 64) gemvg_kernel(const GemvParams p, int
     nr += same ? 1 : 0;
     same &= same - 1;
   }
-  if (nr == 1) gemvg_body<F, KW, R, S, WPG, 1>(p, tok, nr, e, red);
-  else if (nr == 2) gemvg_body<F, KW, R, S, WPG, 2>(p, tok, nr, e, red);
-  else gemvg_body<F, KW, R, S, WPG, 4>(p, tok, nr, e, red);
+  if (nr == 1) gemvg_body<F, KW, R, S, WPG, 1, ONE>(p, tok, nr, e, red);
+  else if (nr == 2) gemvg_body<F, KW, R, S, WPG, 2, ONE>(p, tok, nr, e, red);
+  else gemvg_body<F, KW, R, S, WPG, 4, ONE>(p, tok, nr, e, red);
 }
 
 // Measured on MI355X (graph replay, cold weights, nvfp4 4096 x 4096, us per
@@ -699,8 +736,8 @@ hipError_t run(const QWeight &w, int64_t m, const void *x, void *out, int ot, co
   return hipGetLastError();
 }
 
-// The grouped decode form: the one-round geometry of run(), one grid row per
-// possible tile.
+// The grouped decode form: the geometry of run(), one grid row per possible
+// tile.
 template <int F>
 hipError_t run_grouped(const QWeight &w, int64_t m, int64_t nexp, const int32_t *eids, const void *x, void *out,
                        int ot, int *status, hipStream_t s) {
@@ -716,18 +753,21 @@ hipError_t run_grouped(const QWeight &w, int64_t m, int64_t nexp, const int32_t 
   // tiles: sum over the D routed experts of ceil(rows / T) <= (m + (T - 1) D) / T, D <= min(E, m); and <= m
   constexpr int T = kGemvGroupRows;
   const int64_t tiles = std::min<int64_t>(m, (m + (T - 1) * std::min(nexp, m)) / T);
-  hipLaunchKernelGGL((gemvg_kernel<F, KW, R, S, WPG>), dim3((unsigned)wgs, (unsigned)tiles), dim3(WPG * 64), 0, s,
-                     p, (int)m);
+  if (p.C == 64 * KW)
+    hipLaunchKernelGGL((gemvg_kernel<F, KW, R, S, WPG, true>), dim3((unsigned)wgs, (unsigned)tiles), dim3(WPG * 64),
+                       0, s, p, (int)m);
+  else
+    hipLaunchKernelGGL((gemvg_kernel<F, KW, R, S, WPG, false>), dim3((unsigned)wgs, (unsigned)tiles), dim3(WPG * 64),
+                       0, s, p, (int)m);
   return hipGetLastError();
 }
 
 }  // namespace
 
 bool gemv_grouped_applies(const QWeight &w, int64_t m, int64_t nexp) {
-  // decode-sized m, the one-round shape (64 chunks per wave of the k split), 31-bit offsets
-  const bool k4 = is_4bit(w.fmt);
-  const int64_t E = k4 ? 32 : 16, KW = k4 ? 2 : 4, rowb = k4 ? w.k / 2 : w.k;
-  return m >= 1 && m <= kGemvGroupMaxRows && w.k == 64 * KW * E && w.n * nexp * rowb < ((int64_t)1 << 31) &&
+  // decode-sized m, whole 16-byte code chunks, 31-bit offsets of the stacked weight and of x
+  const int64_t E = is_4bit(w.fmt) ? 32 : 16, rowb = is_4bit(w.fmt) ? w.k / 2 : w.k;
+  return m >= 1 && m <= kGemvGroupMaxRows && w.k >= E && w.k % E == 0 && w.n * nexp * rowb < ((int64_t)1 << 31) &&
          m * w.k < ((int64_t)1 << 30);
 }
 

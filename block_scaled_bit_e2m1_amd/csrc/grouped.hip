@@ -15,9 +15,9 @@
 //     is outside [0, E) are written as zeros and flag *status.
 //  2. mfma_kernel in its grouped form (mfma.hip): X rows gathered and output
 //     rows scattered through the table; tiles past the count exit at once.
-// Decode-sized m on the decode GEMV shapes skips both: the GEMV kernel's
-// grouped form (gemv.hip) routes the few rows itself and streams each
-// expert's weight once per tile of up to 4 of its rows.
+// Decode-sized m (at most 32 rows, 31-bit offsets) skips both: the GEMV
+// kernel's grouped form (gemv.hip) routes the few rows itself and streams
+// each expert's weight once per tile of up to 4 of its rows.
 // The order of rows inside an expert's group comes from LDS atomics, but every
 // output row is computed the same way wherever it sits, so the result is
 // bit-for-bit the same from run to run.

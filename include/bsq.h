@@ -210,9 +210,10 @@ bsq_status bsq_gather_qmm(bsq_format fmt, int block, int64_t m, int64_t n, int64
  * lowp_scaled_grouped_matmul (the expert-indexed GEMM)], computed with the
  * rows grouped by expert: a routing pass on the device sorts the rows by
  * expert into a table in `workspace`, then the bf16 MFMA kernel runs 128-row
- * tiles of each expert's rows; for decode-sized m <= 32 with k = 4096, the
- * decode GEMV kernel routes the rows itself (the workspace is not touched)
- * and runs tiles of up to 4 rows of one expert.  Either way each expert's
+ * tiles of each expert's rows; for decode-sized m <= 32 (and a stacked
+ * weight under 2 GiB of codes) the decode GEMV kernel routes the rows itself
+ * (the workspace is not touched) and runs tiles of up to 4 rows of one
+ * expert.  Either way each expert's
  * weight is streamed once per tile instead of once per row.  x: device bf16
  * [m,k], 16-byte aligned (bf16 only).  expert_ids: device int32 [m].  out:
  * device [m,n] (ot).

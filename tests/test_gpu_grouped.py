@@ -5,9 +5,9 @@ so the oracle is oracle.gather_matmul on the same seeded inputs, to the
 bf16 bound |gpu - ref| <= 2e-3 * sum|x*w| per output.  The cases span experts
 with no rows, one row, a ragged multiple of the 128-row tile, ragged n and k
 (both tile configurations), the largest expert count, ids outside the stack,
-graph replay, the decode form (m <= 32, k = 4096: routed inside the GEMV
-kernel) with shared, lone and bad ids, and the prefill MoE workload at full
-size on sampled rows.  The
+graph replay, the decode form (m <= 32: routed inside the GEMV kernel, one
+round or guarded rounds of the k split) with shared, lone and bad ids, and
+the prefill MoE workload at full size on sampled rows.  The
 output and the workspace sit between guard bands that must come back
 untouched.
 """
@@ -125,9 +125,9 @@ def test_grouped_parity_more_than_one_round(fmt):
 
 @pytest.mark.parametrize("fmt", ALL)
 def test_grouped_decode_form(fmt):
-    """m <= 32 routed rows on the decode GEMV shape (k = 4096) take the
-    decode form (routed in the kernel, tiles of up to 4 rows of one expert,
-    one weight pass per tile): 4 experts of 1000 x 4096 (ragged against every
+    """m <= 32 routed rows take the decode form (routed in the kernel, tiles
+    of up to 4 rows of one expert, one weight pass per tile); at k = 4096 its
+    one-round kernel: 4 experts of 1000 x 4096 (ragged against every
     row group) with rows shared between tokens; m = 1, 5 (tiles of 2 and 3
     rows), 19 (an expert with 9 rows spans three tiles) and 32; bf16 and f32
     output."""
@@ -144,16 +144,23 @@ def test_grouped_decode_form(fmt):
             check_bound(out, ref, den, 2e-3, f"grouped decode {fmt} m={len(ids)} {dt}", dt == torch.bfloat16)
 
 
-def test_grouped_small_m_off_the_decode_shape():
-    """m <= 32 with k other than 4096 keeps the 128-row MFMA tiles: 3 experts
-    of 300 x 512, 7 rows."""
-    E, n, k = 3, 300, 512
-    p, stack = _stack("nvfp4", E, n, k, seed=66)
-    ids = _ids_with_counts([3, 0, 4], seed=67)
-    X = workloads.random_activations(len(ids), k, seed=68, act="bf16")
-    out, st = _run(stack, E, ids, X)
-    assert st == 0
-    _check("nvfp4", p, X, ids, n, out, what="small m, k = 512")
+@pytest.mark.parametrize("fmt", ALL)
+@pytest.mark.parametrize("k", [64, 4160, 14336])
+def test_grouped_decode_form_any_k(fmt, k):
+    """The decode form away from k = 4096: guarded rounds of the k split.
+    k = 64 (fewer chunks than one round, some waves add nothing), 4160 (one
+    full round and a partial one) and 14336 (3.5 rounds, an MoE down
+    projection's k); 4 experts of 300 rows, 9 routed rows in tiles of 4 + 1,
+    3 and 1; bf16 and f32 output."""
+    E, n = 4, 300
+    p, stack = _stack(fmt, E, n, k, seed=69)
+    ids = _ids_with_counts([5, 0, 3, 1], seed=70)
+    X = workloads.random_activations(len(ids), k, seed=71, act="bf16")
+    ref, den = oracle.gather_matmul(X, oracle.dequant_packed(p), ids, n)
+    for dt in (torch.bfloat16, torch.float32):
+        out, st = _run(stack, E, ids, X, dt)
+        assert st == 0
+        check_bound(out, ref, den, 2e-3, f"grouped decode {fmt} k={k} {dt}", dt == torch.bfloat16)
 
 
 def test_grouped_decode_form_bad_ids_and_equal_to_gather():
