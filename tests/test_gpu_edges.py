@@ -146,7 +146,8 @@ def test_e8m0_extreme_bytes_every_kernel(fmt):
     """E8M0 bytes 0..8 (2^-127 is an f32 subnormal), 250..254 and 255 (NaN)
     through the decode GEMV (bf16 x), the streaming kernel (f32 x, and m = 3
     bf16), the bf16 MFMA kernel (whose weight conversion takes the scale byte
-    as an exponent-only operand) and, as the weight of the scaled MFMA GEMM."""
+    as an exponent-only operand), the grouped decode form (tiles of 4 and 2
+    rows) and, as the weight of the scaled MFMA GEMM."""
     rng = np.random.default_rng(77)
     n, k, m = 80, 512, 40
     for name, codes, scales, xs in _extreme_cases(fmt, n, k, rng):
@@ -165,6 +166,13 @@ def test_e8m0_extreme_bytes_every_kernel(fmt):
         for od in (torch.float32, torch.bfloat16):
             out, b = _run(d, X, "bf16", bsq.PATH_MFMA, od)
             _check(out, ref, den, 2e-3, f"{fmt} {name} mfma {od}", b)
+        # the expert-grouped decode form: the weight as 2 experts of n / 2 rows, tiles of 4 and 2 rows
+        ids = np.array([0, 1, 0, 0, 1, 0], np.int32)
+        rg, dg = oracle.gather_matmul(X[:6], wd, ids, n // 2)
+        xg = torch.from_numpy(X[:6]).to(torch.bfloat16).to(DEV)
+        for od in (torch.float32, torch.bfloat16):
+            out = bsq.grouped_qmm(d, 2, torch.from_numpy(ids).to(DEV), xg, out_dtype=od).float().cpu().numpy()
+            _check(out, rg, dg, 2e-3, f"{fmt} {name} grouped decode form {od}", od == torch.bfloat16)
         # scaled MFMA: X packed with the same MX format (ordinary scales)
         xq = bsq.quantize(fmt, torch.from_numpy(X).to(torch.bfloat16).to(DEV))
         px = oracle.pack(fmt, X)
