@@ -505,17 +505,18 @@ __global__ void __launch_bounds__(WPG * 64) gemv1_kernel(const GemvParams p) {
 // weight rows serves up to T of the rows routed to it, where the per-row
 // gather streams the expert once per routed row.
 //
-// The routing is done in the kernel (m <= 64: every id fits one wave): each
-// wave loads the ids, counts for every row the earlier rows of the same
-// expert, and takes as tile leaders the valid rows whose count is a multiple
-// of T; a tile is its leader and the next T - 1 rows (in row order) of the
-// leader's expert.  Grid y enumerates the leaders (WGs past their number exit
-// at once); all of it is uniform, in scalar registers.  Rows whose id is
-// outside [0, E) are zeroed by the workgroups of y = 0 and set *status to 1.
+// The routing is done in the kernel (m <= 32): each wave reads the ids
+// through the scalar unit, lane j counts the earlier rows with row j's
+// expert, and the valid rows whose count is a multiple of T become tile
+// leaders (one ballot); a tile is its leader and the next T - 1 rows (in row
+// order) of the leader's expert, found from ballots, so the tile is uniform.
+// Grid y enumerates the leaders; workgroups past their number exit after the
+// id loads.  Rows whose id is outside [0, E) are zeroed by the workgroups of
+// y = 0, which set *status to 1.
 //
 // Each tile runs the body for its own row count (1, 2 or 4 rows; 3 takes the
-// 4-row body with its last row repeated and not stored), so a lone row costs
-// what the per-row kernel does.  Same geometry as the per-row kernels: one
+// 4-row body with its last row repeated and not stored), so a lone row does
+// one row's loads and arithmetic.  Same geometry as the per-row kernels: one
 // round when k is 64 chunks per wave of the k split (k = 4096), else
 // guarded rounds as in gemv_kernel.  Every lane holds its chunk's activations
 // of the tile's rows, and the weight chunk is decoded once for all of them
