@@ -94,7 +94,8 @@ bsq_status matmul(bsq_path path, bsq_format fmt, int block, int64_t m, int64_t n
   if (!aligned(x, 16)) return fail(BSQ_ERR_ALIGN, "x must be 16-byte aligned");
   if (m > ((int64_t)1 << 40) / k) return fail(BSQ_ERR_SHAPE, "m*k too large");
   const bsq::QWeight w{(int)fmt, n, k, codes, scales, biases, global_scale};
-  if (path == BSQ_PATH_AUTO) path = (xt == BSQ_BF16 && m > 8) ? BSQ_PATH_MFMA : BSQ_PATH_ROWS;
+  if (path == BSQ_PATH_AUTO)
+    path = (xt == BSQ_BF16 && m > 8 && !bsq::gemv_dense_preferred(w, m)) ? BSQ_PATH_MFMA : BSQ_PATH_ROWS;
   if (path == BSQ_PATH_MFMA) return hip_status(bsq::launch_mfma(w, m, x, out, (int)ot, st), "mfma launch");
   return hip_status(bsq::launch_rows(w, m, x, (int)xt, out, (int)ot, st), "rows launch");
 }

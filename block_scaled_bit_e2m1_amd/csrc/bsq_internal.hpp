@@ -75,9 +75,17 @@ hipError_t launch_gemv_norm(const QWeight &w, const void *x, const void *gam, fl
 // their rows and set *status (may be null) to 1.  Applies to m up to
 // kGemvGroupMaxRows, whole 16-byte code chunks, and 31-bit offsets of the
 // stacked weight and of the m rows.
+// With eids null the same kernel runs m dense rows of one weight (nexp 1) in
+// tiles of kGemvGroupRows consecutive rows: the small-m bf16 product takes it
+// for 2 <= m <= kGemvDenseRows.
 constexpr int kGemvGroupRows = 4;
 constexpr int64_t kGemvGroupMaxRows = 32;
+constexpr int64_t kGemvDenseRows = 32;
 bool gemv_grouped_applies(const QWeight &w, int64_t m, int64_t nexp);
+// Whether bf16 X of m rows is better served by that multi-row form than by
+// the MFMA kernel (measured crossover: m <= 8, or m <= 32 while ceil(m/4)
+// passes over the packed weight stay within 96 MB).
+bool gemv_dense_preferred(const QWeight &w, int64_t m);
 hipError_t launch_gemv_grouped(const QWeight &w, int64_t m, int64_t nexp, const int32_t *eids, const void *x,
                                void *out, int ot, int *status, hipStream_t s);
 // MFMA kernel: bf16 X, any m >= 1.

@@ -630,48 +630,59 @@ __global__ void __launch_bounds__(WPG * 64) gemvg_kernel(const GemvParams p, int
   constexpr int T = kGemvGroupRows, RG = WPG / KW, RS = R * S;
   static_assert(KW > 1 && T == 4 && RS * T <= 64, "the k-split combine stores one sum per lane");
   __shared__ float red[WPG][RS * T];
-  constexpr int MM = (int)kGemvGroupMaxRows;
-  const int lane = threadIdx.x & 63;
-  // The ids through the scalar unit: uniform loads that, after the first
-  // workgroup on a CU, hit its scalar cache, so a workgroup with no tile
-  // leaves after a short wait.  Lane j takes row j's expert and counts the
-  // earlier rows of the same expert.
-  int ids[MM];
+  int tok[4], nr, e;
+  if (!p.eids) {
+    // dense rows of one weight (no routing): tile y is rows 4y .. 4y + 3 below m
+    const int r0 = blockIdx.y * T;
+    nr = min(T, m - r0);
 #pragma unroll
-  for (int j = 0; j < MM; ++j) ids[j] = j < m ? p.eids[j] : -1;
-  int el = -1, rank = 0;
+    for (int t = 0; t < 4; ++t) tok[t] = r0 + min(t, nr - 1);
+    e = 0;
+  } else {
+    constexpr int MM = (int)kGemvGroupMaxRows;
+    const int lane = threadIdx.x & 63;
+    // The ids through the scalar unit: uniform loads that, after the first
+    // workgroup on a CU, hit its scalar cache, so a workgroup with no tile
+    // leaves after a short wait.  Lane j takes row j's expert and counts the
+    // earlier rows of the same expert.
+    int ids[MM];
 #pragma unroll
-  for (int j = 0; j < MM; ++j) el = lane == j ? ids[j] : el;
+    for (int j = 0; j < MM; ++j) ids[j] = j < m ? p.eids[j] : -1;
+    int el = -1, rank = 0;
 #pragma unroll
-  for (int j = 0; j < MM; ++j) rank += (j < lane && ids[j] == el) ? 1 : 0;
-  const bool valid = lane < m && el >= 0 && (int64_t)el < p.nexp;
-  if (blockIdx.y == 0) {
-    const uint64_t bad = __ballot(lane < m && !valid);
-    if (bad) {
-      if (p.status && blockIdx.x == 0 && threadIdx.x == 0) *p.status = 1;
-      const int c0 = blockIdx.x * RG * RS, n = (int)p.n;
-      for (uint64_t b = bad; b; b &= b - 1) {
-        const int i = __builtin_ctzll(b);
-        for (int c = threadIdx.x; c < RG * RS && c0 + c < n; c += WPG * 64) {
-          const size_t o = (size_t)i * (size_t)n + c0 + c;
-          if (p.ot == 0) reinterpret_cast<float *>(p.out)[o] = 0.0f;
-          else reinterpret_cast<uint16_t *>(p.out)[o] = 0;
+    for (int j = 0; j < MM; ++j) el = lane == j ? ids[j] : el;
+#pragma unroll
+    for (int j = 0; j < MM; ++j) rank += (j < lane && ids[j] == el) ? 1 : 0;
+    const bool valid = lane < m && el >= 0 && (int64_t)el < p.nexp;
+    if (blockIdx.y == 0) {
+      const uint64_t bad = __ballot(lane < m && !valid);
+      if (bad) {
+        if (p.status && blockIdx.x == 0 && threadIdx.x == 0) *p.status = 1;
+        const int c0 = blockIdx.x * RG * RS, n = (int)p.n;
+        for (uint64_t b = bad; b; b &= b - 1) {
+          const int i = __builtin_ctzll(b);
+          for (int c = threadIdx.x; c < RG * RS && c0 + c < n; c += WPG * 64) {
+            const size_t o = (size_t)i * (size_t)n + c0 + c;
+            if (p.ot == 0) reinterpret_cast<float *>(p.out)[o] = 0.0f;
+            else reinterpret_cast<uint16_t *>(p.out)[o] = 0;
+          }
         }
       }
     }
-  }
-  uint64_t lead = __ballot(valid && rank % T == 0);
-  if ((int)blockIdx.y >= __popcll(lead)) return;  // uniform: no tile for this y
-  for (unsigned q = 0; q < blockIdx.y; ++q) lead &= lead - 1;
-  const int p0 = __builtin_ctzll(lead);
-  const int e = __builtin_amdgcn_readlane(el, p0);
-  uint64_t same = (__ballot(valid && el == e) >> p0) & ~(uint64_t)1;  // the expert's rows after the leader
-  int tok[4] = {p0, p0, p0, p0}, nr = 1;
+    uint64_t lead = __ballot(valid && rank % T == 0);
+    if ((int)blockIdx.y >= __popcll(lead)) return;  // uniform: no tile for this y
+    for (unsigned q = 0; q < blockIdx.y; ++q) lead &= lead - 1;
+    const int p0 = __builtin_ctzll(lead);
+    e = __builtin_amdgcn_readlane(el, p0);
+    uint64_t same = (__ballot(valid && el == e) >> p0) & ~(uint64_t)1;  // the expert's rows after the leader
+    tok[0] = tok[1] = tok[2] = tok[3] = p0;
+    nr = 1;
 #pragma unroll
-  for (int t = 1; t < 4; ++t) {
-    tok[t] = same ? p0 + __builtin_ctzll(same) : tok[t - 1];
-    nr += same ? 1 : 0;
-    same &= same - 1;
+    for (int t = 1; t < 4; ++t) {
+      tok[t] = same ? p0 + __builtin_ctzll(same) : tok[t - 1];
+      nr += same ? 1 : 0;
+      same &= same - 1;
+    }
   }
   if (nr == 1) gemvg_body<F, KW, R, S, WPG, 1, ONE>(p, tok, nr, e, red);
   else if (nr == 2) gemvg_body<F, KW, R, S, WPG, 2, ONE>(p, tok, nr, e, red);
@@ -751,9 +762,10 @@ hipError_t run_grouped(const QWeight &w, int64_t m, int64_t nexp, const int32_t 
   p.eids = eids;
   p.nexp = nexp;
   p.status = status;
-  // tiles: sum over the D routed experts of ceil(rows / T) <= (m + (T - 1) D) / T, D <= min(E, m); and <= m
+  // routed tiles: sum over the D routed experts of ceil(rows / T) <= (m + (T - 1) D) / T, D <= min(E, m);
+  // and <= m.  Dense rows (no ids): ceil(m / T) tiles.
   constexpr int T = kGemvGroupRows;
-  const int64_t tiles = std::min<int64_t>(m, (m + (T - 1) * std::min(nexp, m)) / T);
+  const int64_t tiles = eids ? std::min<int64_t>(m, (m + (T - 1) * std::min(nexp, m)) / T) : (m + T - 1) / T;
   if (p.C == 64 * KW)
     hipLaunchKernelGGL((gemvg_kernel<F, KW, R, S, WPG, true>), dim3((unsigned)wgs, (unsigned)tiles), dim3(WPG * 64),
                        0, s, p, (int)m);
@@ -770,6 +782,15 @@ bool gemv_grouped_applies(const QWeight &w, int64_t m, int64_t nexp) {
   const int64_t E = is_4bit(w.fmt) ? 32 : 16, rowb = is_4bit(w.fmt) ? w.k / 2 : w.k;
   return m >= 1 && m <= kGemvGroupMaxRows && w.k >= E && w.k % E == 0 && w.n * nexp * rowb < ((int64_t)1 << 31) &&
          m * w.k < ((int64_t)1 << 30);
+}
+
+bool gemv_dense_preferred(const QWeight &w, int64_t m) {
+  if (m > kGemvDenseRows || !gemv_grouped_applies(w, m, 1)) return false;
+  if (m <= 8) return true;
+  // packed bytes of the weight: codes, scales (and int4 biases)
+  const int64_t B = block_of(w.fmt), sb = (w.fmt == kNVFP8 || w.fmt == kINT8_SYM) ? 4 : (w.fmt == kINT4_AFFINE ? 2 : 1);
+  const int64_t row = (is_4bit(w.fmt) ? w.k / 2 : w.k) + (w.k / B) * sb + (w.fmt == kINT4_AFFINE ? (w.k / B) * 2 : 0);
+  return (m + kGemvGroupRows - 1) / kGemvGroupRows * w.n * row <= (int64_t)96 << 20;
 }
 
 hipError_t launch_gemv_grouped(const QWeight &w, int64_t m, int64_t nexp, const int32_t *eids, const void *x,

@@ -468,6 +468,9 @@ hipError_t launch(const QWeight &w, int64_t m, const void *x, int xt, void *out,
 hipError_t launch_rows(const QWeight &w, int64_t m, const void *x, int xt, void *out, int ot, hipStream_t s) {
   // one bf16 activation row: the decode GEMV kernel (gemv.hip)
   if (gemv_applies(w, m, xt, false)) return launch_gemv(w, m, x, out, ot, nullptr, 0, nullptr, s);
+  // a few bf16 rows: its multi-row form, one weight pass per 4 rows (gemv.hip)
+  if (xt == 1 && m <= kGemvDenseRows && gemv_grouped_applies(w, m, 1))
+    return launch_gemv_grouped(w, m, 1, nullptr, x, out, ot, nullptr, s);
   return launch<false>(w, m, x, xt, out, ot, nullptr, 0.0f, Route{nullptr, 0, nullptr}, s);
 }
 

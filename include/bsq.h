@@ -82,7 +82,7 @@ typedef int bsq_dtype;
 /* Kernel family selector for bsq_qgemm_path. */
 enum {
     BSQ_PATH_AUTO = 0,  /* library choice by shape and dtype */
-    BSQ_PATH_ROWS = 1,  /* VALU streaming kernel: W decoded once, FMA against every X row */
+    BSQ_PATH_ROWS = 1,  /* VALU streaming kernels: W decoded in registers, dotted with the X rows */
     BSQ_PATH_MFMA = 2   /* LDS-tiled bf16 MFMA kernel (bf16 X only) */
 };
 typedef int bsq_path;
@@ -157,8 +157,11 @@ bsq_status bsq_qgemv(bsq_format fmt, int block, int64_t n, int64_t k, const void
 
 /* Multi-row quantized matmul: out[i,j] = sum_p X[i,p] * dequant(W)[j,p]
  * [metaltile PR #250, qmm commit and "mt_mxfp4_qmm_mma" (the M >= 32 path);
- *  metaltile-std src/mlx/fp_quantized_mma.rs, mt_fp4_qmm_mma].  Small m and
- * f32 X use the streaming kernel, larger bf16 m the MFMA kernel. */
+ *  metaltile-std src/mlx/fp_quantized_mma.rs, mt_fp4_qmm_mma].  f32 X uses
+ * the streaming kernel; bf16 X with m <= 8, or m <= 32 where ceil(m/4) passes
+ * over the packed weight stay within 96 MB, the decode GEMV kernel's
+ * multi-row form (one weight pass per 4 rows); larger bf16 m the MFMA
+ * kernel. */
 bsq_status bsq_qgemm(bsq_format fmt, int block, int64_t m, int64_t n, int64_t k, const void *codes,
                      const void *scales, const void *biases, float global_scale, const void *x, bsq_dtype xt,
                      void *out, bsq_dtype ot, void *stream);

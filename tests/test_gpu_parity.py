@@ -213,6 +213,35 @@ def test_qgemm_rows_parity(fmt, act):
 
 
 @pytest.mark.parametrize("fmt", ALL)
+@pytest.mark.parametrize("k", [4096, 576])
+def test_qgemm_small_m_multirow_form(fmt, k):
+    """bf16 X with a few rows (the default path: tiles of up to 4 rows on the
+    decode GEMV kernel, one weight pass per tile): m = 2, 3, 5, 8 and 17 (17
+    still takes it for a weight this small), k = 4096 (one round of the k
+    split) and 576 (guarded rounds), n = 300 ragged against the 16-row
+    workgroups.  Every output meets the oracle bound, stays inside its guard
+    bands, and (f32 out) equals the one-row GEMV of the same row bit for bit:
+    the same chunk order and reductions."""
+    n = 300
+    W = workloads.random_weights(n, k, seed=k + 7, sigma=0.02)
+    p, d = packed(fmt, W)
+    wd = oracle.dequant_packed(p)
+    for m in (2, 3, 5, 8, 17):
+        X = workloads.random_activations(m, k, seed=k + m, act="bf16")
+        ref, den = oracle.matmul(X, wd)
+        xt = torch.from_numpy(X).to(torch.bfloat16).to(DEV)
+        for od in (torch.float32, torch.bfloat16):
+            buf, out = guarded((m, n), od)
+            bsq.qgemm(d, xt, out=out)
+            check_guard(buf, m * n, f"{fmt} m={m} k={k} {od}")
+            o = out.float().cpu().numpy()
+            check_bound(o, ref, den, 2e-3, f"multi-row {fmt} m={m} k={k} {od}", od == torch.bfloat16)
+            if od == torch.float32:
+                rows = np.stack([bsq.qgemv(d, xt[i], out_dtype=torch.float32).cpu().numpy() for i in range(m)])
+                assert same_bits(o, rows).all(), f"{fmt} m={m} k={k}: multi-row form differs from the one-row GEMV"
+
+
+@pytest.mark.parametrize("fmt", ALL)
 def test_qgemm_mfma_parity(fmt):
     for m, n, k in [(1, 72, 256), (40, 300, 1024), (200, 130, 192), (257, 129, 64 * 5 + (32 if BLOCK[fmt] <= 32 else 0))]:
         if k % BLOCK[fmt]:
