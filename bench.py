@@ -436,6 +436,32 @@ def time_moe_decode_shared(device, fmt="mxfp4", E=8, n=14336, k=4096, ids=(1, 6,
             "roofline_frac": round(wb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "us_per_launch_gather": round(us_gather, 3)}
 
 
+def time_small_m(device, fmt="mxfp4", n=14336, k=4096, m=4):
+    """Batched decode (a few bf16 rows, bsq_qgemm's default path: the decode
+    GEMV kernel's multi-row form, one weight pass per 4 rows) against the
+    MFMA path on the same call.  Rate = packed weight bytes per launch / time
+    (ceil(m/4) passes stream it); the weight copies rotated span 640 MB."""
+    import torch
+
+    from block_scaled_bit_e2m1_amd import bsq, workloads
+
+    pw = bsq.pack(fmt, workloads.random_weights(n, k, seed=1007, sigma=0.02))
+    copies = max(2, min(32, ROTATE_BYTES // pw.weight_bytes + 1))
+    ws = [bsq.to_device(pw, device) for _ in range(copies)]
+    x = torch.from_numpy(workloads.random_activations(m, k, seed=1008, act="bf16")).to(torch.bfloat16).to(device)
+    out = torch.empty((m, n), dtype=torch.bfloat16, device=device)
+    it, it2 = iter(range(1 << 62)), iter(range(1 << 62))
+    reps = max(1, 400 // copies)
+    us = graph_event_ms(lambda: bsq.qgemm(ws[next(it) % copies], x, out=out), copies, reps, device) * 1e3
+    us_mfma = graph_event_ms(lambda: bsq.qgemm(ws[next(it2) % copies], x, out=out, path=bsq.PATH_MFMA), copies,
+                             reps, device) * 1e3
+    wb = pw.weight_bytes
+    return {"workload": f"qgemm_small_m_{fmt}_{n}x{k}_m{m}",
+            "note": "batched decode: default path (multi-row GEMV form) vs the MFMA path",
+            "value": round(wb / (us * 1e-6) / 1e9, 2), "unit": "GB/s", "us_per_launch": round(us, 3),
+            "roofline_frac": round(wb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "us_per_launch_mfma": round(us_mfma, 3)}
+
+
 def time_grouped_qmm(device, name="mxfp4_moe_prefill_8x4096", reps=200):
     """Prefill MoE step (bsq_grouped_qgemm): the routing kernel, then the
     grouped MFMA GEMM over 128-row tiles of each expert's rows, bf16 out.  One
@@ -729,10 +755,12 @@ def main():
 
     if not args.no_extra and not args.only_timed:
         extra.append(time_quantize(device))
-        for e in (time_rmsnorm_qgemv(device), time_gather_qmm(device), time_moe_decode_shared(device)):
+        for e in (time_rmsnorm_qgemv(device), time_gather_qmm(device), time_moe_decode_shared(device),
+                  time_small_m(device)):
             extra.append(e)
             log(f"  {e['workload']}: {e['value']:.1f} GB/s ({e['us_per_launch']:.2f} us/launch)"
-                + (f", per-row gather {e['us_per_launch_gather']:.2f} us" if 'us_per_launch_gather' in e else ""))
+                + (f", per-row gather {e['us_per_launch_gather']:.2f} us" if 'us_per_launch_gather' in e else "")
+                + (f", MFMA path {e['us_per_launch_mfma']:.2f} us" if 'us_per_launch_mfma' in e else ""))
         torch.cuda.empty_cache()
         e = time_grouped_qmm(device)
         extra.append(e)
