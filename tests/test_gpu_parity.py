@@ -251,6 +251,18 @@ def test_qgemm_mfma_parity(fmt):
 
 
 @pytest.mark.parametrize("fmt", ALL)
+def test_qgemm_mfma_small_row_tiles(fmt):
+    """The MFMA kernel's 32-row (m <= 32) and 64-row (m <= 64) tiles: m = 7,
+    32, 33 and 64 across ragged n and k, bf16 and f32 output, in guard
+    bands."""
+    ragged_k = 64 * 5 + (32 if BLOCK[fmt] <= 32 else 0)
+    for m, n, k in [(7, 300, ragged_k), (32, 129, 1024), (33, 70, ragged_k), (64, 1000, 576)]:
+        for od in (torch.float32, torch.bfloat16):
+            out, ref, den, b = run_matmul(fmt, m, n, k, "bf16", bsq.PATH_MFMA, seed=m + n, out_dtype=od)
+            check_bound(out, ref, den, 2e-3, f"mfma small tiles {fmt} m={m} n={n} k={k} {od}", b)
+
+
+@pytest.mark.parametrize("fmt", ALL)
 def test_qgemm_mfma_wide_tiles(fmt):
     """Problems with at least 128 tiles of 128x256 (the wide tiling): k a
     multiple of 256 (scales loaded per 256-k trip: one trip, several trips and
