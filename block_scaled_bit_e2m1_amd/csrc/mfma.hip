@@ -818,13 +818,19 @@ hipError_t run_f(const QWeight &w, int64_t m, const void *x, void *out, int ot, 
   // smaller problems use 128x64 tiles, ~3 workgroups per CU, and m <= 64
   // rows the 32- or 64-row tiles of the same schedule, so that the MFMAs do
   // not run 128 rows for a few (mxfp4 14336 x 4096, m = 16 / 64: 35.1 / 34.9
-  // -> 22.2 / 27.9 us; int8 11008 x 4096, m = 16: 58.4 -> 38.5 us).
+  // -> 22.2 / 27.9 us; int8 11008 x 4096, m = 16: 58.4 -> 38.5 us).  64-row
+  // tiles also take over while the 128x64 grid would give at most half a
+  // tile per CU (mxfp4 4096 x 4096, m = 96..256: 33.8-34.2 -> 26.3-27.3 us);
+  // with more tiles than that, each extra m-tile's second decode of the
+  // weight costs more than the fuller grid gains (mxfp4 14336 x 4096, m = 96:
+  // 36.6 vs 47.0 us).
   const int64_t wide = ((m + 127) / 128) * ((w.n + 255) / 256);
   const int64_t tall = ((m + 255) / 256) * ((w.n + 127) / 128);
+  const int64_t small = ((m + 127) / 128) * ((w.n + 63) / 64);
   if (w.n >= 256 && wide >= 128) return run_cfg<F, 128, 256, 1, 8, 1, 4, false, 5>(w, m, x, out, ot, s);
   if (tall >= 128) return run_cfg<F, 256, 128, 2, 4, 1, 4, false, 5>(w, m, x, out, ot, s);
   if (m <= 32) return run_cfg<F, 32, 64, 1, 2, 2, 4, false, 4>(w, m, x, out, ot, s);
-  if (m <= 64) return run_cfg<F, 64, 64, 2, 2, 2, 4, false, 4>(w, m, x, out, ot, s);
+  if (m <= 64 || small <= 128) return run_cfg<F, 64, 64, 2, 2, 2, 4, false, 4>(w, m, x, out, ot, s);
   return run_cfg<F, 128, 64, 2, 2, 2, 4, false, 4>(w, m, x, out, ot, s);
 }
 
