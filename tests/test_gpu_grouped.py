@@ -109,6 +109,23 @@ def test_grouped_parity_wide_tiles(fmt, k):
 
 
 @pytest.mark.parametrize("fmt", ALL)
+def test_grouped_parity_few_rows_per_expert(fmt):
+    """Few rows per expert on the 128-row MFMA tiles: 8 experts of 300 x 512
+    with 100 rows (experts of 30, 33 and 1 rows, empty experts) and 4
+    experts with 200 rows (70, 64, 1, 65); every row, bf16 and f32 output."""
+    n, k = 300, 512
+    for E, counts, seed in ((8, [30, 0, 1, 33, 12, 24, 0, 0], 75), (4, [70, 64, 1, 65], 78)):
+        p, stack = _stack(fmt, E, n, k, seed=seed)
+        ids = _ids_with_counts(counts, seed=seed + 1)
+        X = workloads.random_activations(len(ids), k, seed=seed + 2, act="bf16")
+        ref, den = oracle.gather_matmul(X, oracle.dequant_packed(p), ids, n)
+        for dt in (torch.bfloat16, torch.float32):
+            out, st = _run(stack, E, ids, X, dt)
+            assert st == 0
+            check_bound(out, ref, den, 2e-3, f"grouped few rows {fmt} E={E} m={len(ids)} {dt}", dt == torch.bfloat16)
+
+
+@pytest.mark.parametrize("fmt", ALL)
 def test_grouped_parity_more_than_one_round(fmt):
     """8 experts of 3900 x 256 with 2100 rows: more than 256 wide tiles, where
     the float formats switch to 128x128 tiles (two workgroups per CU) and
