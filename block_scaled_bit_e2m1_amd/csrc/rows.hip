@@ -1,5 +1,7 @@
-// rows.hip -- VALU streaming kernel for the decode GEMV (m = 1) and for small
-// m / f32 activations: out[i,j] = sum_p X[i,p] * dequant(W)[j,p].
+// rows.hip -- VALU streaming kernel for f32 activations (any m, routed or not), the fused
+// RMSNorm beyond the one-row bf16 case, and bf16 rows the decode GEMV kernel
+// (gemv.hip) does not take (stacks of 2 GiB of codes or more):
+// out[i,j] = sum_p X[i,p] * dequant(W)[j,p].
 //
 // The weight stream is the cost ("the win is memory bandwidth, not flops,
 // since LLM weights dominate the working set" [rlx-cpu quant.rs,
