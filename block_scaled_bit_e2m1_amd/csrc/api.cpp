@@ -222,7 +222,7 @@ bsq_status bsq_rmsnorm_qgemv(bsq_format fmt, int block, int64_t m, int64_t n, in
   if (m > ((int64_t)1 << 40) / k) return fail(BSQ_ERR_SHAPE, "m*k too large");
   const bsq::QWeight w{(int)fmt, n, k, codes, scales, biases, global_scale};
   if (bsq::gemv_norm_applies(w, m, (int)xt))
-    return hip_status(bsq::launch_gemv_norm(w, x, norm_weight, eps, out, (int)ot, st), "rmsnorm gemv launch");
+    return hip_status(bsq::launch_gemv_norm(w, m, x, norm_weight, eps, out, (int)ot, st), "rmsnorm gemv launch");
   return hip_status(bsq::launch_rows_norm(w, m, x, (int)xt, norm_weight, eps, out, (int)ot, st), "rmsnorm rows launch");
 }
 

@@ -64,10 +64,12 @@ hipError_t launch_rows_gather(const QWeight &w, int64_t m, const void *x, int xt
 bool gemv_applies(const QWeight &w, int64_t m, int xt, bool routed);
 hipError_t launch_gemv(const QWeight &w, int64_t m, const void *x, void *out, int ot, const int32_t *eids,
                        int64_t nexp, int *status, hipStream_t s);
-// The fused RMSNorm on the decode GEMV kernel: one bf16 row, k = 64 chunks per
-// wave of the k split (4096 for every format).
+// The fused RMSNorm on the decode GEMV kernel: up to kGemvNormRows bf16 rows
+// (one grid row each), k = 64 chunks per wave of the k split (4096 for every
+// format).
+constexpr int64_t kGemvNormRows = 32;
 bool gemv_norm_applies(const QWeight &w, int64_t m, int xt);
-hipError_t launch_gemv_norm(const QWeight &w, const void *x, const void *gam, float eps, void *out, int ot,
+hipError_t launch_gemv_norm(const QWeight &w, int64_t m, const void *x, const void *gam, float eps, void *out, int ot,
                             hipStream_t s);
 // The decode form of the expert-grouped matmul on the decode GEMV kernel
 // (gemv.hip): routed in the kernel itself, tiles of up to kGemvGroupRows rows

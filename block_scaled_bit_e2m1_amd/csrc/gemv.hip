@@ -738,7 +738,7 @@ hipError_t run(const QWeight &w, int64_t m, const void *x, void *out, int ot, co
   const bool one = p.C == 64 * KW;
   const dim3 grid((unsigned)wgs, (unsigned)m), block(WPG * 64);
   if (gam) {  // the fused RMSNorm: the one-round kernel only (checked by gemv_norm_applies)
-    if (!(o32 && one) || m != 1) return hipErrorInvalidValue;
+    if (!(o32 && one)) return hipErrorInvalidValue;
     hipLaunchKernelGGL((gemv1_kernel<F, KW, R, S, WPG, true>), grid, block, 0, s, p);
     return hipGetLastError();
   }
@@ -814,22 +814,24 @@ bool gemv_applies(const QWeight &w, int64_t m, int xt, bool routed) {
 }
 
 bool gemv_norm_applies(const QWeight &w, int64_t m, int xt) {
-  // one bf16 row, one full round of 16-byte chunks per wave (k = 4096), 31-bit offsets
+  // up to kGemvNormRows bf16 rows (one grid row each; their weight passes meet in the caches),
+  // one full round of 16-byte chunks per wave (k = 4096), 31-bit offsets
   const bool k4 = is_4bit(w.fmt);
   const int64_t E = k4 ? 32 : 16, KW = k4 ? 2 : 4;
-  return xt == 1 && m == 1 && w.k == 64 * KW * E && w.n * (k4 ? w.k / 2 : w.k) < ((int64_t)1 << 31);
+  return xt == 1 && m >= 1 && m <= kGemvNormRows && w.k == 64 * KW * E &&
+         w.n * (k4 ? w.k / 2 : w.k) < ((int64_t)1 << 31);
 }
 
-hipError_t launch_gemv_norm(const QWeight &w, const void *x, const void *gam, float eps, void *out, int ot,
+hipError_t launch_gemv_norm(const QWeight &w, int64_t m, const void *x, const void *gam, float eps, void *out, int ot,
                             hipStream_t s) {
   switch (w.fmt) {
-    case kMXFP4: return run<kMXFP4>(w, 1, x, out, ot, nullptr, 0, nullptr, s, gam, eps);
-    case kNVFP4: return run<kNVFP4>(w, 1, x, out, ot, nullptr, 0, nullptr, s, gam, eps);
-    case kMXFP8_E4M3: return run<kMXFP8_E4M3>(w, 1, x, out, ot, nullptr, 0, nullptr, s, gam, eps);
-    case kMXFP8_E5M2: return run<kMXFP8_E5M2>(w, 1, x, out, ot, nullptr, 0, nullptr, s, gam, eps);
-    case kNVFP8: return run<kNVFP8>(w, 1, x, out, ot, nullptr, 0, nullptr, s, gam, eps);
-    case kINT4_AFFINE: return run<kINT4_AFFINE>(w, 1, x, out, ot, nullptr, 0, nullptr, s, gam, eps);
-    case kINT8_SYM: return run<kINT8_SYM>(w, 1, x, out, ot, nullptr, 0, nullptr, s, gam, eps);
+    case kMXFP4: return run<kMXFP4>(w, m, x, out, ot, nullptr, 0, nullptr, s, gam, eps);
+    case kNVFP4: return run<kNVFP4>(w, m, x, out, ot, nullptr, 0, nullptr, s, gam, eps);
+    case kMXFP8_E4M3: return run<kMXFP8_E4M3>(w, m, x, out, ot, nullptr, 0, nullptr, s, gam, eps);
+    case kMXFP8_E5M2: return run<kMXFP8_E5M2>(w, m, x, out, ot, nullptr, 0, nullptr, s, gam, eps);
+    case kNVFP8: return run<kNVFP8>(w, m, x, out, ot, nullptr, 0, nullptr, s, gam, eps);
+    case kINT4_AFFINE: return run<kINT4_AFFINE>(w, m, x, out, ot, nullptr, 0, nullptr, s, gam, eps);
+    case kINT8_SYM: return run<kINT8_SYM>(w, m, x, out, ot, nullptr, 0, nullptr, s, gam, eps);
   }
   return hipErrorInvalidValue;
 }

@@ -621,6 +621,30 @@ def test_rmsnorm_qgemv_parity(fmt):
         check_bound(out, ref, den, tol, f"rmsnorm_qgemv {fmt} m={m} n={n} k={k} {act}", act == "bf16")
 
 
+@pytest.mark.parametrize("fmt", ALL)
+def test_rmsnorm_qgemv_few_rows_one_round(fmt):
+    """k = 4096 with 2, 5, 8 and 17 bf16 rows takes the one-round fused kernel,
+    one grid row per activation row: every output meets the oracle bound and
+    (f32 out) equals the m = 1 call on that row bit for bit."""
+    n, k = 300, 4096
+    W = workloads.random_weights(n, k, seed=21, sigma=0.02)
+    pw = bsq.to_device(bsq.pack(fmt, W), DEV)
+    wd = oracle.dequant_packed(oracle.pack(fmt, W))
+    g = _gain(k, 22, "bf16")
+    gt = torch.from_numpy(g).to(torch.bfloat16).to(DEV)
+    for m in (2, 5, 8, 17):
+        X = workloads.random_activations(m, k, seed=23 + m, act="bf16")
+        ref, den = oracle.matmul(oracle.rmsnorm(X, g, 1e-6), wd)
+        x = torch.from_numpy(X).to(torch.bfloat16).to(DEV)
+        buf, o = guarded((m, n), torch.float32)
+        bsq.rmsnorm_qgemv(pw, x, gt, 1e-6, out=o)
+        check_guard(buf, m * n, f"rmsnorm_qgemv {fmt} m={m}")
+        out = o.cpu().numpy()
+        check_bound(out, ref, den, 2e-3, f"rmsnorm_qgemv {fmt} m={m} k=4096")
+        rows = np.stack([bsq.rmsnorm_qgemv(pw, x[i], gt, 1e-6, out_dtype=torch.float32).cpu().numpy() for i in range(m)])
+        assert same_bits(out, rows).all(), f"{fmt} m={m}: rows differ from the one-row fused call"
+
+
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp8_e4m3", "int4_affine"])
 def test_rmsnorm_qgemv_lds_limit(fmt):
     """One bf16 row: x*g is staged in LDS up to k = 8192; k = 8192 takes that
