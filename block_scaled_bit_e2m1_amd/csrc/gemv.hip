@@ -135,23 +135,33 @@ __device__ __forceinline__ float chunk_dot(v4u c, uint32_t s, uint32_t b, const 
     const f32x2_t sv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(s, 1.0f, false);
     acc = __builtin_fmaf(p0, sv[0], acc);
     return __builtin_fmaf(p1, sv[1], acc);
-  } else if constexpr (Traits<F>::kBits == 4) {  // mxfp4, int4: one scale (group) per chunk
+  } else if constexpr (F == kINT4_AFFINE) {
+    // Each nibble pair becomes the exact bf16 pair (128 + q_even, 128 + q_odd)
+    // (exponent 2^7, the nibble in the low mantissa bits): one byte permute
+    // and an OR, then v_dot2 against x; 128 * sum(x) comes off afterwards,
+    // sum(x) itself (for the bias) being v_dot2 against ones.
+    const uint32_t wv[4] = {c.x, c.y, c.z, c.w};
+    float p = 0.0f, xs = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t lo = wv[u] & 0x0F0F0F0Fu, hi = (wv[u] >> 4) & 0x0F0F0F0Fu;
+      const uint32_t xv[4] = {xq[u].x, xq[u].y, xq[u].z, xq[u].w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t pr =
+            __builtin_amdgcn_perm(hi, lo, (0x0Cu << 24) | ((4u + t) << 16) | (0x0Cu << 8) | (uint32_t)t) | 0x43004300u;
+        p = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pr), as_bf16x2(xv[t]), p, false);
+        xs = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(0x3F803F80u), as_bf16x2(xv[t]), xs, false);
+      }
+    }
+    acc = __builtin_fmaf(__builtin_fmaf(-128.0f, xs, p), block_scale<F>(s), acc);
+    return __builtin_fmaf(xs, bf16_bits_to_f32(b), acc);
+  } else if constexpr (Traits<F>::kBits == 4) {  // mxfp4: one scale per chunk
     float p = dot8_bf16<F>(c.x, 0u, xq[0], 0.0f);
     p = dot8_bf16<F>(c.y, 0u, xq[1], p);
     p = dot8_bf16<F>(c.z, 0u, xq[2], p);
     p = dot8_bf16<F>(c.w, 0u, xq[3], p);
-    acc = __builtin_fmaf(p, block_scale<F>(s), acc);
-    if constexpr (F == kINT4_AFFINE) {
-      float xs = 0.0f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t v[4] = {xq[q].x, xq[q].y, xq[q].z, xq[q].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) xs += __uint_as_float(v[i] << 16) + __uint_as_float(v[i] & 0xFFFF0000u);
-      }
-      acc = __builtin_fmaf(xs, bf16_bits_to_f32(b), acc);
-    }
-    return acc;
+    return __builtin_fmaf(p, block_scale<F>(s), acc);
   } else {  // 8-bit codes: 16 elements, one scale
     float p = dot8_bf16<F>(c.x, c.y, xq[0], 0.0f);
     p = dot8_bf16<F>(c.z, c.w, xq[1], p);
