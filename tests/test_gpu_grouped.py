@@ -284,7 +284,8 @@ def test_grouped_degenerate_and_rejected():
 
 def test_grouped_graph_replay():
     """Routing and matmul captured in a HIP graph: every replay, with eager
-    work between replays, equals the eager result."""
+    work between replays, equals the eager result; so does the decode form
+    (12 rows, routed inside the kernel, one bad id) in the same graph."""
     E, n, k = 5, 320, 512
     _, stack = _stack("mxfp8_e5m2", E, n, k, seed=131)
     ids = np.random.default_rng(132).integers(0, E, 400).astype(np.int32)
@@ -294,22 +295,33 @@ def test_grouped_graph_replay():
     ws = torch.empty(need, dtype=torch.uint8, device=DEV)
     ref = bsq.grouped_qmm(stack, E, eids, x, workspace=ws).clone()
     out = torch.empty_like(ref)
+    dids = torch.tensor([4, 0, 4, 2, 9, 4, 0, 1, 4, 2, 3, 4], dtype=torch.int32, device=DEV)  # 9 is outside [0, 5)
+    dx = x[:12]
+    dws = torch.empty(max(bsq.bsq_grouped_qgemm_workspace(12, E)[1], 4), dtype=torch.uint8, device=DEV)
+    dst = torch.zeros(1, dtype=torch.int32, device=DEV)
+    dref = bsq.grouped_qmm(stack, E, dids, dx, workspace=dws).clone()
+    dout = torch.empty_like(dref)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         bsq.grouped_qmm(stack, E, eids, x, out=out, workspace=ws)
+        bsq.grouped_qmm(stack, E, dids, dx, out=dout, workspace=dws, status=dst)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=s):
         bsq.grouped_qmm(stack, E, eids, x, out=out, workspace=ws)
+        bsq.grouped_qmm(stack, E, dids, dx, out=dout, workspace=dws, status=dst)
     for _ in range(3):
         out.fill_(0)
+        dout.fill_(7)
+        dst.zero_()
         ws.fill_(0xFF)
         bsq.qgemv(stack, x[:1])  # eager work between replays
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref)
+        assert torch.equal(dout, dref) and (dout[4] == 0).all() and int(dst.item()) == bsq.ERR_ARG
 
 
 def test_grouped_workload_moe_prefill_sampled():

@@ -424,21 +424,26 @@ def test_graph_replay_matches_eager():
         x = torch.from_numpy(X).to(torch.bfloat16).to(DEV)
         e_v = bsq.qgemv(d, x[0]).clone()
         e_m = bsq.qgemm(d, x).clone()
+        e_s = bsq.qgemm(d, x[:5]).clone()  # a few rows: the multi-row GEMV form
         s = torch.cuda.Stream()
         gv = torch.empty_like(e_v)
         gm = torch.empty_like(e_m)
+        gs = torch.empty_like(e_s)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=s):
             bsq.qgemv(d, x[0], out=gv)
             bsq.qgemm(d, x, out=gm)
+            bsq.qgemm(d, x[:5], out=gs)
         for rep in range(4):
             gv.fill_(float("nan"))
             gm.fill_(float("nan"))
+            gs.fill_(float("nan"))
             g.replay()
             torch.cuda.synchronize()
             assert torch.equal(gv, e_v), (fmt, rep)
             assert torch.equal(gm, e_m), (fmt, rep)
+            assert torch.equal(gs, e_s), (fmt, rep)
             bsq.qgemm(d, x[:7])  # eager work between replays
             torch.cuda.synchronize()
         outs[fmt] = True
