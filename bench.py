@@ -20,6 +20,7 @@ for the timed kernel, and the CPU oracle timed on a bounded sample as
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-extra] [--no-cpu] [--only-timed] [--mx-only] [--grouped-only] [--moe-decode-only]
+                    [--small-m-only]
 """
 from __future__ import annotations
 
@@ -632,6 +633,8 @@ def main():
     ap.add_argument("--grouped-only", action="store_true", help="only time the prefill MoE grouped GEMM and exit")
     ap.add_argument("--moe-decode-only", action="store_true",
                     help="only time the decode MoE with shared experts (grouped call vs gather) and exit")
+    ap.add_argument("--small-m-only", action="store_true",
+                    help="only time the batched-decode qgemm (a few bf16 rows: default path vs MFMA) and exit")
     ap.add_argument("--mx-pair", default="", help="with --mx-only: one pair XFMT,WFMT (e.g. mxfp4,mxfp4)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="only run torch's copy kernel on MIB MiB (counter calibration) and exit")
@@ -685,6 +688,9 @@ def main():
         return
     if args.moe_decode_only:
         print(json.dumps(time_moe_decode_shared(device)), flush=True)
+        return
+    if args.small_m_only:
+        print(json.dumps(time_small_m(device)), flush=True)
         return
     if args.grouped_only:
         print(json.dumps(time_grouped_qmm(device, reps=max(4, args.steps))), flush=True)
